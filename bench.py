@@ -1,0 +1,276 @@
+"""Benchmark of the block-sparse cross-scale attention hot path on one MI355X.
+
+One step = one pass of the CSLA hot path over the batch of the 2B-shaped last
+scale: build the block mask and its kept-tile lists (varsparse_build_mask),
+then block-sparse attention of the 64 x 64 query scale over the 10521-token
+multi-scale cache (varsparse_attn_fwd), B = 2 (CFG pair), H = 16, d = 128,
+bf16.  Inputs are synthetic (seeded spatial fields), resident in HBM before the
+timed region.
+
+value = effective TFLOP/s: 4 d |Q| |K| summed over the kept (query tile, key
+tile) pairs with real token counts, per step, divided by the step time.  The
+dense kernel written with the same tile engine is timed on the same tensors
+for the speedup; the CS4A path (decision-scale scoring + selection + mapping +
+attention at sides 40/48/64) is timed as a second line item.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cs4a", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def tile_sizes(sides, q_scale, t):
+    """Token count of every key tile of scales 0..q_scale (id order)."""
+    out = []
+    for s in range(q_scale + 1):
+        h = sides[s]
+        nb = -(-h // t)
+        for a in range(nb):
+            for b in range(nb):
+                out.append(min(t, h - a * t) * min(t, h - b * t))
+    return np.array(out, np.int64)
+
+
+def kept_flops(cnt, idx, sizes, q_tile_tokens, d, heads):
+    """4 d |Q| |K| over the kept pairs of shared (heads > 0) or per-head lists."""
+    cnt = cnt.reshape(-1, cnt.shape[-1]) if cnt.ndim > 1 else cnt[None]
+    idx = idx.reshape(-1, *idx.shape[-2:]) if idx.ndim > 2 else idx[None]
+    total = 0
+    for c, ix in zip(cnt, idx):
+        for r in range(c.shape[0]):
+            total += int(sizes[ix[r, : c[r]]].sum())
+    mult = heads if cnt.shape[0] == 1 else 1
+    return 4.0 * d * q_tile_tokens * total * mult
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import block_sparse_cross_csla_amd as vs
+    from varsparse_inputs import SpatialField, bf16_bits, round_bf16, workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(bf16_bits(x)).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    w = W.LAST_SCALE_2B
+    f = SpatialField(w.seed, w.wid, w.B, w.H, w.d)
+    k_np, v_np = f.keys_values(w.sides[: w.q_scale + 1], w.n_sink, largest_side=w.sides[w.q_scale])
+    q_np = f.queries(w.sides[w.q_scale])
+    q, k, v = to_dev(q_np), to_dev(k_np), to_dev(v_np)
+    nqb, nkb, nq, nk = vs.geom_counts(w.sides, w.tile, w.q_scale)
+    kv_cnt = torch.empty(nqb, dtype=torch.int32, device=dev)
+    kv_idx = torch.empty(nqb, nkb, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, nq, dtype=torch.float32, device=dev)
+    od = torch.empty_like(q)
+    lsed = torch.empty_like(lse)
+    scale = 1.0 / math.sqrt(w.d)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, radius=w.radii, out=(kv_cnt, kv_idx, None), stream=stream)
+        vs.attn_fwd(q, k, v, w.sides, w.tile, w.q_scale, kv_cnt, kv_idx, softmax_scale=scale, out=o, lse=lse,
+                    stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # timed region: K whole steps, HIP events around every launch on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, radius=w.radii, out=(kv_cnt, kv_idx, None), stream=stream)
+        ev[i][1].record(stream)
+        vs.attn_fwd(q, k, v, w.sides, w.tile, w.q_scale, kv_cnt, kv_idx, softmax_scale=scale, out=o, lse=lse,
+                    stream=stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    mask_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]))
+    attn_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]))
+    print(f"[bench] sparse steps done: {ms_step:.4f} ms/step, attn {attn_ms:.4f} ms", file=sys.stderr, flush=True)
+
+    sizes = tile_sizes(w.sides, w.q_scale, w.tile)
+    cnt_h, idx_h = kv_cnt.cpu().numpy(), kv_idx.cpu().numpy()
+    flops = kept_flops(cnt_h, idx_h, sizes, w.tile * w.tile, w.d, w.B * w.H)
+    dense_flops = 4.0 * w.d * nq * nk * w.B * w.H
+    count_sparsity = 1.0 - cnt_h.sum() / (nqb * nkb)
+    flop_sparsity = 1.0 - flops / dense_flops
+
+    # dense comparator on the same tensors
+    nd = max(3, args.steps // 5)
+    for _ in range(2):
+        vs.dense_attn_fwd(q, k, v, softmax_scale=scale, out=od, lse=lsed, stream=stream)
+    torch.cuda.synchronize()
+    de = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nd)]
+    for i in range(nd):
+        de[i][0].record(stream)
+        vs.dense_attn_fwd(q, k, v, softmax_scale=scale, out=od, lse=lsed, stream=stream)
+        de[i][1].record(stream)
+    torch.cuda.synchronize()
+    dense_ms = float(np.mean([de[i][0].elapsed_time(de[i][1]) for i in range(nd)]))
+    print(f"[bench] dense done: {dense_ms:.4f} ms", file=sys.stderr, flush=True)
+
+    result = {
+        "metric": "last-scale sparse-attn effective TFLOP/s + speedup vs dense attn, 1 MI355X",
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "last_scale_2b", "B": w.B, "H": w.H, "head_dim": w.d, "query_side": w.sides[w.q_scale],
+                   "query_tokens": nq, "cached_tokens": nk, "scales": list(w.sides), "tile": w.tile,
+                   "n_sink": w.n_sink, "radius": w.radius, "mask": "csla"},
+        "speedup_vs_dense": dense_ms / ms_step,
+        "kernel_speedup_vs_dense": dense_ms / attn_ms,
+        "attn_kernel_ms": attn_ms,
+        "mask_kernel_ms": mask_ms,
+        "dense_kernel_ms": dense_ms,
+        "dense_tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
+        "block_sparsity": {"count": float(count_sparsity), "flop": float(flop_sparsity)},
+        "roofline": {"bound": "mfma", "achieved": flops / (attn_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "traffic": None, "kernel": "attn_fwd_bf16_kernel<128,false>",
+                     "flop_per_launch": flops},
+    }
+
+    if not args.no_cs4a:
+        result["cs4a"] = bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev)
+        print("[bench] cs4a done", file=sys.stderr, flush=True)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q_np, k_np, v_np, cnt_h, idx_h, sizes, round_bf16, args.cpu_seconds)
+        print("[bench] cpu baseline done", file=sys.stderr, flush=True)
+    print(json.dumps(result), flush=True)
+
+
+def bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev):
+    """Score at side 32, select top-p 0.9, map to sides 40/48/64, attend at each."""
+    w = W.CS4A
+    D = W.CS4A_DECISION
+    f = SpatialField(w.seed, w.wid, w.B, w.H, w.d)
+    k_np, v_np = f.keys_values(w.sides[: w.q_scale + 1], w.n_sink, largest_side=w.sides[w.q_scale])
+    k, v = to_dev(k_np), to_dev(v_np)
+    q_d = to_dev(f.queries(w.sides[D]))
+    qs = {T: to_dev(f.queries(w.sides[T])) for T in W.CS4A_TARGETS}
+    scores = torch.empty(w.B, w.H, *vs.geom_counts(w.sides, w.tile, D)[:2], dtype=torch.float32, device=dev)
+    lists, outs, nks = {}, {}, {}
+    for T in W.CS4A_TARGETS:
+        nqb, nkb, nq, nk = vs.geom_counts(w.sides, w.tile, T)
+        lists[T] = (torch.empty(w.B, w.H, nqb, dtype=torch.int32, device=dev),
+                    torch.empty(w.B, w.H, nqb, nkb, dtype=torch.int32, device=dev))
+        outs[T] = torch.empty_like(qs[T])
+        nks[T] = nk
+    scale = 1.0 / math.sqrt(w.d)
+
+    def step():
+        for i, T in enumerate(W.CS4A_TARGETS):
+            vs.map_indices(w.sides, w.tile, D, T, w.n_sink, W.CS4A_TOP_P, q_d=q_d if i == 0 else None,
+                           k=k, scores=scores, out=lists[T], stream=stream)
+        for T in W.CS4A_TARGETS:
+            vs.attn_fwd(qs[T], k[:, :, : nks[T]], v[:, :, : nks[T]], w.sides, w.tile, T, *lists[T],
+                        softmax_scale=scale, out=outs[T], want_lse=False, stream=stream)
+
+    def dense_step():
+        for T in W.CS4A_TARGETS:
+            vs.dense_attn_fwd(qs[T], k[:, :, : nks[T]], v[:, :, : nks[T]], softmax_scale=scale, out=outs[T],
+                              want_lse=False, stream=stream)
+
+    n = max(5, args.steps // 2)
+    res = {}
+    for name, fn in (("sparse", step), ("dense", dense_step)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / n
+    flops = 0.0
+    for T in W.CS4A_TARGETS:
+        sizes = tile_sizes(w.sides, T, w.tile)
+        flops += kept_flops(lists[T][0].cpu().numpy(), lists[T][1].cpu().numpy(), sizes, w.tile * w.tile, w.d, 0)
+    nqb_D, nkb_D = scores.shape[2:]
+    return {"workload": "cs4a_2b", "B": w.B, "H": w.H, "decision_side": w.sides[D],
+            "target_sides": [w.sides[T] for T in W.CS4A_TARGETS], "top_p": W.CS4A_TOP_P,
+            "ms_per_step": res["sparse"], "dense_ms_per_step": res["dense"],
+            "speedup_vs_dense": res["dense"] / res["sparse"],
+            "attention_tflop_per_step": flops / 1e12,
+            "effective_tflops": flops / (res["sparse"] * 1e-3) / 1e12,
+            "timed": "score + select + map (3 targets) + 3 block-sparse attentions; dense: 3 dense attentions"}
+
+
+def cpu_baseline(w, q_np, k_np, v_np, cnt_h, idx_h, sizes, round_bf16, seconds):
+    """The oracle (numpy float64 masked dense softmax attention) on a bounded
+    sample of the same workload: (query tile, head) pairs in order until about
+    ``seconds`` of CPU work, scaled to effective TFLOP/s."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention as OA
+    done, flops = 0, 0.0
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        q = round_bf16(q_np[b:b + 1, h:h + 1]).astype(np.float64)
+        k = round_bf16(k_np[b:b + 1, h:h + 1]).astype(np.float64)
+        v = round_bf16(v_np[b:b + 1, h:h + 1]).astype(np.float64)
+        for tile in range(cnt_h.shape[0]):
+            if time.perf_counter() - t0 >= seconds:
+                break
+            OA.block_sparse_attention(q, k, v, w.sides, w.q_scale, w.tile, cnt_h, idx_h, 1 / math.sqrt(w.d),
+                                      q_tiles=[tile])
+            flops += 4.0 * w.d * w.tile * w.tile * int(sizes[idx_h[tile, : cnt_h[tile]]].sum())
+            done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {cnt_h.shape[0] * len(heads)} (query tile, head) pairs in order, {el:.1f} s, "
+                      f"numpy float64, host of {os.cpu_count()} logical CPUs"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,24 @@
+"""Block-sparse cross-scale attention (SparVAR's CSLA / CS4A hot path) for
+AMD Instinct MI355X (gfx950).
+
+The computation runs in libvarsparse.so (HIP kernels behind the C ABI of
+include/varsparse.h); this package only marshals arguments.  Importing it
+fails if the library has not been built.
+"""
+from ._lib import (  # noqa: F401
+    BF16,
+    EHIP,
+    EINVAL,
+    EUNSUPPORTED,
+    FP32,
+    LIB_PATH,
+    OK,
+    VarsparseError,
+    attn_fwd,
+    build_mask,
+    dense_attn_fwd,
+    geom_counts,
+    lib,
+    make_geom,
+    map_indices,
+)

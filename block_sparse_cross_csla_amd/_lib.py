@@ -1,0 +1,215 @@
+"""ctypes binding of libvarsparse (include/varsparse.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch supplies device memory (outputs are
+allocated here with torch.empty) and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarsparse.so")
+MAX_SCALES = 32
+BF16, FP32 = 0, 1
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
+
+EXPORTS = (
+    "varsparse_geom_counts",
+    "varsparse_build_mask",
+    "varsparse_map_indices",
+    "varsparse_attn_fwd",
+    "varsparse_dense_attn_fwd",
+    "varsparse_strerror",
+    "varsparse_last_hip_error",
+)
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [("n_scales", ctypes.c_int32), ("side", ctypes.c_int32 * MAX_SCALES), ("tile", ctypes.c_int32)]
+
+
+class VarsparseError(RuntimeError):
+    def __init__(self, code: int, where: str, hip: int = 0):
+        self.code = code
+        msg = f"{where}: {_LIB.varsparse_strerror(code).decode()} ({code})"
+        if code == EHIP:
+            msg += f", hipError {hip}"
+        super().__init__(msg)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_cross_csla_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    PI32, PI64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    PG = ctypes.POINTER(Geom)
+    lib.varsparse_geom_counts.argtypes = [PG, I32, PI32, PI32, PI64, PI64]
+    lib.varsparse_build_mask.argtypes = [PG, I32, I32, PI32, I32, P, P, P, P]
+    lib.varsparse_map_indices.argtypes = [PG, I32, I32, I32, F32, I32, I32, I32, I32,
+                                          P, PI64, P, PI64, F32, P, P, P, P, P, P]
+    lib.varsparse_attn_fwd.argtypes = [PG, I32, I32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32, P]
+    lib.varsparse_dense_attn_fwd.argtypes = [I32, I32, I32, I32, I64, I64, P, P, P, P, P, PI64, F32, P]
+    lib.varsparse_strerror.argtypes = [ctypes.c_int]
+    lib.varsparse_strerror.restype = ctypes.c_char_p
+    lib.varsparse_last_hip_error.argtypes = []
+    for name in EXPORTS[:5]:
+        getattr(lib, name).restype = ctypes.c_int
+    lib.varsparse_last_hip_error.restype = ctypes.c_int
+    return lib
+
+
+_LIB = _load()
+
+
+def lib():
+    return _LIB
+
+
+def _check(rc: int, where: str):
+    if rc != OK:
+        raise VarsparseError(rc, where, _LIB.varsparse_last_hip_error() if rc == EHIP else 0)
+
+
+def make_geom(sides, tile: int) -> Geom:
+    g = Geom()
+    g.n_scales = len(sides)
+    for i, s in enumerate(sides):
+        g.side[i] = int(s)
+    g.tile = int(tile)
+    return g
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _strides(*tensors):
+    vals = []
+    for t in tensors:
+        if t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+        vals.extend(t.stride()[:3])
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def geom_counts(sides, tile: int, q_scale: int):
+    """(nqb, nkb, nq, nk) of a query scale (host only)."""
+    g = make_geom(sides, tile)
+    nqb, nkb = ctypes.c_int32(), ctypes.c_int32()
+    nq, nk = ctypes.c_int64(), ctypes.c_int64()
+    _check(_LIB.varsparse_geom_counts(ctypes.byref(g), q_scale, ctypes.byref(nqb), ctypes.byref(nkb),
+                                      ctypes.byref(nq), ctypes.byref(nk)), "varsparse_geom_counts")
+    return nqb.value, nkb.value, nq.value, nk.value
+
+
+def build_mask(sides, tile: int, q_scale: int, n_sink: int, radius=None, budget: int = -1,
+               want_mask: bool = False, device="cuda", out=None, stream=None):
+    """CSLA kept-tile lists: (kv_cnt int32 [nqb], kv_idx int32 [nqb, nkb], mask uint8 [nqb, nkb] or None).
+    ``out`` may pass preallocated (kv_cnt, kv_idx, mask)."""
+    nqb, nkb, _, _ = geom_counts(sides, tile, q_scale)
+    if out is None:
+        kv_cnt = torch.empty(nqb, dtype=torch.int32, device=device)
+        kv_idx = torch.empty(nqb, nkb, dtype=torch.int32, device=device)
+        mask = torch.empty(nqb, nkb, dtype=torch.uint8, device=device) if want_mask else None
+    else:
+        kv_cnt, kv_idx, mask = out
+    g = make_geom(sides, tile)
+    rad = None
+    if radius is not None:
+        rad = (ctypes.c_int32 * (q_scale + 1))(*[int(r) for r in radius[: q_scale + 1]])
+    _check(_LIB.varsparse_build_mask(ctypes.byref(g), q_scale, n_sink, rad, budget, _ptr(mask),
+                                     _ptr(kv_cnt), _ptr(kv_idx), _stream(stream)), "varsparse_build_mask")
+    return kv_cnt, kv_idx, mask
+
+
+def map_indices(sides, tile: int, d_scale: int, t_scale: int, n_sink: int, top_p: float,
+                q_d=None, k=None, softmax_scale=None, scores=None, want_selection=False, out=None, stream=None):
+    """CS4A: scores (computed when q_d is given, else taken from ``scores``),
+    selection and per-(b,h) target lists.  Returns (scores, sel_cnt, sel_idx, kv_cnt, kv_idx)."""
+    if q_d is not None:
+        B, H, _, d = q_d.shape
+        device = q_d.device
+    else:
+        B, H = scores.shape[:2]
+        d = 0
+        device = scores.device
+    nqbD, nkbD, _, _ = geom_counts(sides, tile, d_scale)
+    nqbT, nkbT, _, _ = geom_counts(sides, tile, t_scale)
+    if scores is None:
+        scores = torch.empty(B, H, nqbD, nkbD, dtype=torch.float32, device=device)
+    if out is None:
+        kv_cnt = torch.empty(B, H, nqbT, dtype=torch.int32, device=device)
+        kv_idx = torch.empty(B, H, nqbT, nkbT, dtype=torch.int32, device=device)
+    else:
+        kv_cnt, kv_idx = out
+    sel_cnt = sel_idx = None
+    if want_selection:
+        sel_cnt = torch.empty(B, H, nqbD, dtype=torch.int32, device=device)
+        sel_idx = torch.empty(B, H, nqbD, nkbD, dtype=torch.int32, device=device)
+    g = make_geom(sides, tile)
+    if q_d is not None:
+        scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+        qs = (ctypes.c_int64 * 3)(*q_d.stride()[:3])
+        ks = (ctypes.c_int64 * 3)(*k.stride()[:3])
+        if q_d.stride(-1) != 1 or k.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+        dt = _dtype_code(q_d)
+    else:
+        scale, qs, ks, dt = 1.0, None, None, BF16
+    _check(_LIB.varsparse_map_indices(ctypes.byref(g), d_scale, t_scale, n_sink, float(top_p), dt, B, H, d,
+                                      _ptr(q_d), qs, _ptr(k), ks, float(scale), _ptr(scores),
+                                      _ptr(sel_cnt), _ptr(sel_idx), _ptr(kv_cnt), _ptr(kv_idx), _stream(stream)),
+           "varsparse_map_indices")
+    return scores, sel_cnt, sel_idx, kv_cnt, kv_idx
+
+
+def attn_fwd(q, k, v, sides, tile: int, q_scale: int, kv_cnt, kv_idx, softmax_scale=None,
+             out=None, lse=None, want_lse=True, stream=None):
+    """Block-sparse attention; q [B,H,side^2,d], k/v [B,H,Nk,d].  Lists shared
+    (kv_cnt [nqb]) or per (b,h) (kv_cnt [B,H,nqb]).  Returns (o, lse)."""
+    B, H, nq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, nq, dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    per_head = 1 if kv_cnt.dim() == 3 else 0
+    g = make_geom(sides, tile)
+    _check(_LIB.varsparse_attn_fwd(ctypes.byref(g), q_scale, _dtype_code(q), B, H, d, _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(out), _ptr(lse), _strides(q, k, v, out), float(scale), _ptr(kv_cnt),
+                                   _ptr(kv_idx), per_head, _stream(stream)), "varsparse_attn_fwd")
+    return out, lse
+
+
+def dense_attn_fwd(q, k, v, softmax_scale=None, out=None, lse=None, want_lse=True, stream=None):
+    """Dense attention with the same tile engine; q [B,H,nq,d], k/v [B,H,nk,d]."""
+    B, H, nq, d = q.shape
+    nk = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, nq, dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    _check(_LIB.varsparse_dense_attn_fwd(_dtype_code(q), B, H, d, nq, nk, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                         _ptr(lse), _strides(q, k, v, out), float(scale), _stream(stream)),
+           "varsparse_dense_attn_fwd")
+    return out, lse

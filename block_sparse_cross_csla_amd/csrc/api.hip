@@ -1,0 +1,249 @@
+// The C ABI of libvarsparse: argument validation on the host, then kernel
+// launches on the caller's stream.  Nothing here allocates device memory.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kernel_args.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return VARSPARSE_OK;
+    g_last_hip = (int)e;
+    return VARSPARSE_EHIP;
+}
+
+// Geometry: 1..32 scales, positive strictly ascending sides, tile >= 1, and a
+// cache small enough for 32-bit token indices.
+int check_geom(const varsparse_geom* g) {
+    if (g == nullptr) return VARSPARSE_EINVAL;
+    if (g->n_scales < 1 || g->n_scales > VARSPARSE_MAX_SCALES || g->tile < 1) return VARSPARSE_EINVAL;
+    int64_t total = 0;
+    for (int s = 0; s < g->n_scales; ++s) {
+        if (g->side[s] < 1 || g->side[s] > 65535) return VARSPARSE_EINVAL;
+        if (s > 0 && g->side[s] <= g->side[s - 1]) return VARSPARSE_EINVAL;
+        total += (int64_t)g->side[s] * g->side[s];
+    }
+    if (total >= (int64_t)1 << 30) return VARSPARSE_EINVAL;
+    return VARSPARSE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool strides_ok(const int64_t* st, int n, int64_t unit) {
+    for (int i = 0; i < n; ++i)
+        if (st[i] < 0 || st[i] % unit != 0) return false;
+    return true;
+}
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.0f; }
+
+constexpr double kLog2e = 1.4426950408889634;
+
+}  // namespace
+
+extern "C" {
+
+int varsparse_geom_counts(const varsparse_geom* geom, int32_t q_scale, int32_t* nqb, int32_t* nkb,
+                          int64_t* nq, int64_t* nk) {
+    int rc = check_geom(geom);
+    if (rc) return rc;
+    if (q_scale < 0 || q_scale >= geom->n_scales) return VARSPARSE_EINVAL;
+    const vs::DevGeom d = vs::make_dev_geom(*geom, q_scale);
+    if (nqb) *nqb = d.nb[q_scale] * d.nb[q_scale];
+    if (nkb) *nkb = d.tile_base[q_scale + 1];
+    if (nq) *nq = (int64_t)geom->side[q_scale] * geom->side[q_scale];
+    if (nk) *nk = d.tok_off[q_scale + 1];
+    return VARSPARSE_OK;
+}
+
+int varsparse_build_mask(const varsparse_geom* geom, int32_t q_scale, int32_t n_sink, const int32_t* radius,
+                         int32_t budget, uint8_t* mask, int32_t* kv_cnt, int32_t* kv_idx, void* stream) {
+    int rc = check_geom(geom);
+    if (rc) return rc;
+    if (q_scale < 0 || q_scale >= geom->n_scales) return VARSPARSE_EINVAL;
+    if (geom->side[q_scale] % geom->tile != 0) return VARSPARSE_EINVAL;
+    if (n_sink < 0 || n_sink > q_scale) return VARSPARSE_EINVAL;
+    if (kv_cnt == nullptr || kv_idx == nullptr) return VARSPARSE_EINVAL;
+    if (budget == 0 || budget < -1) return VARSPARSE_EINVAL;
+    if (budget == -1 && radius == nullptr) return VARSPARSE_EINVAL;
+    vs::MaskArgs a{};
+    a.g = vs::make_dev_geom(*geom, q_scale);
+    a.q_scale = q_scale;
+    a.n_sink = n_sink;
+    a.budget = budget;
+    a.nkb = a.g.tile_base[q_scale + 1];
+    if (budget > 0 && a.nkb > 4096) return VARSPARSE_EUNSUPPORTED;
+    const int sink_tiles = a.g.tile_base[n_sink];
+    a.keep_n = budget > 0 ? (int)std::min<int64_t>(a.nkb, std::max<int64_t>(budget, sink_tiles + 1)) : 0;
+    for (int s = 0; s <= q_scale; ++s) a.radius[s] = budget == -1 ? radius[s] : -1;
+    a.mask = mask;
+    a.kv_cnt = kv_cnt;
+    a.kv_idx = kv_idx;
+    const int nqb = a.g.nb[q_scale] * a.g.nb[q_scale];
+    return hip_status(vs::launch_csla_mask(a, nqb, (hipStream_t)stream));
+}
+
+int varsparse_map_indices(const varsparse_geom* geom, int32_t d_scale, int32_t t_scale, int32_t n_sink,
+                          float top_p, varsparse_dtype dtype, int32_t B, int32_t H, int32_t head_dim,
+                          const void* q_d, const int64_t q_strides[3], const void* k,
+                          const int64_t k_strides[3], float softmax_scale, float* scores,
+                          int32_t* sel_cnt, int32_t* sel_idx, int32_t* kv_cnt, int32_t* kv_idx,
+                          void* stream) {
+    int rc = check_geom(geom);
+    if (rc) return rc;
+    if (d_scale < 0 || t_scale < d_scale || t_scale >= geom->n_scales) return VARSPARSE_EINVAL;
+    if (geom->side[d_scale] % geom->tile != 0 || geom->side[t_scale] % geom->tile != 0) return VARSPARSE_EINVAL;
+    if (n_sink < 0 || n_sink > d_scale) return VARSPARSE_EINVAL;
+    if (!(top_p > 0.0f && top_p <= 1.0f)) return VARSPARSE_EINVAL;
+    if (B < 1 || H < 1) return VARSPARSE_EINVAL;
+    if (scores == nullptr || kv_cnt == nullptr || kv_idx == nullptr) return VARSPARSE_EINVAL;
+    if ((sel_cnt == nullptr) != (sel_idx == nullptr)) return VARSPARSE_EINVAL;
+    const vs::DevGeom gD = vs::make_dev_geom(*geom, d_scale);
+    const vs::DevGeom gT = vs::make_dev_geom(*geom, t_scale);
+    const int nqbD = gD.nb[d_scale] * gD.nb[d_scale], nkbD = gD.tile_base[d_scale + 1];
+    const int nqbT = gT.nb[t_scale] * gT.nb[t_scale], nkbT = gT.tile_base[t_scale + 1];
+    if (nkbD > 256) return VARSPARSE_EUNSUPPORTED;
+    const int words = (nkbD + 31) / 32;
+    if ((int64_t)nqbD * words * 4 > 32768) return VARSPARSE_EUNSUPPORTED;
+    if ((int64_t)B * H > 0x7fffffff / std::max(nqbD, 1)) return VARSPARSE_EINVAL;
+    if (q_d != nullptr) {
+        if (dtype != VARSPARSE_BF16) return VARSPARSE_EUNSUPPORTED;
+        if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;
+        if (geom->tile != 8) return VARSPARSE_EUNSUPPORTED;
+        if (k == nullptr || q_strides == nullptr || k_strides == nullptr) return VARSPARSE_EINVAL;
+        if (!aligned16(q_d) || !aligned16(k)) return VARSPARSE_EINVAL;
+        if (!strides_ok(q_strides, 3, 8) || !strides_ok(k_strides, 3, 8)) return VARSPARSE_EINVAL;
+        if (!scale_ok(softmax_scale)) return VARSPARSE_EINVAL;
+        vs::ScoreArgs sa{};
+        sa.q = (const __bf16*)q_d;
+        sa.k = (const __bf16*)k;
+        sa.scores = scores;
+        sa.sq_b = q_strides[0]; sa.sq_h = q_strides[1]; sa.sq_t = q_strides[2];
+        sa.sk_b = k_strides[0]; sa.sk_h = k_strides[1]; sa.sk_t = k_strides[2];
+        sa.B = B;
+        sa.H = H;
+        sa.scale_log2 = (float)(softmax_scale * kLog2e);
+        sa.d_side = geom->side[d_scale];
+        sa.nqb = nqbD;
+        sa.nkb = nkbD;
+        sa.g = gD;
+        rc = hip_status(vs::launch_cs4a_score(sa, head_dim, (hipStream_t)stream));
+        if (rc) return rc;
+    }
+    vs::SelMapArgs m{};
+    m.g = gT;
+    m.d_scale = d_scale;
+    m.t_scale = t_scale;
+    m.n_sink = n_sink;
+    m.nqbD = nqbD;
+    m.nkbD = nkbD;
+    m.nqbT = nqbT;
+    m.nkbT = nkbT;
+    m.words = words;
+    m.top_p = (double)top_p;
+    m.scores = scores;
+    m.sel_cnt = sel_cnt;
+    m.sel_idx = sel_idx;
+    m.kv_cnt = kv_cnt;
+    m.kv_idx = kv_idx;
+    return hip_status(vs::launch_cs4a_select_map(m, B * H, (hipStream_t)stream));
+}
+
+int varsparse_attn_fwd(const varsparse_geom* geom, int32_t q_scale, varsparse_dtype dtype, int32_t B, int32_t H,
+                       int32_t head_dim, const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int64_t strides[12], float softmax_scale, const int32_t* kv_cnt,
+                       const int32_t* kv_idx, int32_t lists_per_head, void* stream) {
+    int rc = check_geom(geom);
+    if (rc) return rc;
+    if (q_scale < 0 || q_scale >= geom->n_scales) return VARSPARSE_EINVAL;
+    if (geom->side[q_scale] % geom->tile != 0) return VARSPARSE_EINVAL;
+    if (dtype != VARSPARSE_BF16 && dtype != VARSPARSE_FP32) return VARSPARSE_EINVAL;
+    if (B < 1 || H < 1) return VARSPARSE_EINVAL;
+    if (!q || !k || !v || !o || !strides || !kv_cnt || !kv_idx) return VARSPARSE_EINVAL;
+    if (lists_per_head != 0 && lists_per_head != 1) return VARSPARSE_EINVAL;
+    if (!scale_ok(softmax_scale)) return VARSPARSE_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VARSPARSE_EINVAL;
+    if (!strides_ok(strides, 12, dtype == VARSPARSE_BF16 ? 8 : 4)) return VARSPARSE_EINVAL;
+    if (dtype == VARSPARSE_BF16 && geom->tile != 8) return VARSPARSE_EUNSUPPORTED;
+    if (dtype == VARSPARSE_FP32 && geom->tile * geom->tile > 64) return VARSPARSE_EUNSUPPORTED;
+    const vs::DevGeom g = vs::make_dev_geom(*geom, q_scale);
+    const int nqb = g.nb[q_scale] * g.nb[q_scale];
+    if ((int64_t)nqb * B * H > 0x7fffffff) return VARSPARSE_EINVAL;
+    const float sl2 = (float)(softmax_scale * kLog2e);
+    if (dtype == VARSPARSE_BF16) {
+        vs::AttnArgs a{};
+        a.q = (const __bf16*)q; a.k = (const __bf16*)k; a.v = (const __bf16*)v; a.o = (__bf16*)o; a.lse = lse;
+        a.sq_b = strides[0]; a.sq_h = strides[1]; a.sq_t = strides[2];
+        a.sk_b = strides[3]; a.sk_h = strides[4]; a.sk_t = strides[5];
+        a.sv_b = strides[6]; a.sv_h = strides[7]; a.sv_t = strides[8];
+        a.so_b = strides[9]; a.so_h = strides[10]; a.so_t = strides[11];
+        a.B = B; a.H = H; a.scale_log2 = sl2;
+        a.kv_cnt = kv_cnt; a.kv_idx = kv_idx; a.per_head = lists_per_head;
+        a.nqb = nqb; a.nkb = g.tile_base[q_scale + 1]; a.q_side = geom->side[q_scale]; a.g = g;
+        return hip_status(vs::launch_attn_bf16(a, head_dim, false, (hipStream_t)stream));
+    }
+    vs::AttnF32Args a{};
+    a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v; a.o = (float*)o; a.lse = lse;
+    a.sq_b = strides[0]; a.sq_h = strides[1]; a.sq_t = strides[2];
+    a.sk_b = strides[3]; a.sk_h = strides[4]; a.sk_t = strides[5];
+    a.sv_b = strides[6]; a.sv_h = strides[7]; a.sv_t = strides[8];
+    a.so_b = strides[9]; a.so_h = strides[10]; a.so_t = strides[11];
+    a.B = B; a.H = H; a.scale_log2 = sl2;
+    a.kv_cnt = kv_cnt; a.kv_idx = kv_idx; a.per_head = lists_per_head;
+    a.nqb = nqb; a.nkb = g.tile_base[q_scale + 1]; a.q_side = geom->side[q_scale]; a.g = g;
+    return hip_status(vs::launch_attn_fp32(a, head_dim, false, (hipStream_t)stream));
+}
+
+int varsparse_dense_attn_fwd(varsparse_dtype dtype, int32_t B, int32_t H, int32_t head_dim, int64_t nq, int64_t nk,
+                             const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int64_t strides[12], float softmax_scale, void* stream) {
+    if (dtype != VARSPARSE_BF16 && dtype != VARSPARSE_FP32) return VARSPARSE_EINVAL;
+    if (B < 1 || H < 1 || nq < 1 || nk < 1) return VARSPARSE_EINVAL;
+    if (nk >= ((int64_t)1 << 30)) return VARSPARSE_EUNSUPPORTED;
+    if (!q || !k || !v || !o || !strides) return VARSPARSE_EINVAL;
+    if (!scale_ok(softmax_scale)) return VARSPARSE_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VARSPARSE_EINVAL;
+    if (!strides_ok(strides, 12, dtype == VARSPARSE_BF16 ? 8 : 4)) return VARSPARSE_EINVAL;
+    if (((nq + 63) / 64) * B * H > 0x7fffffff) return VARSPARSE_EINVAL;
+    const float sl2 = (float)(softmax_scale * kLog2e);
+    if (dtype == VARSPARSE_BF16) {
+        vs::AttnArgs a{};
+        a.q = (const __bf16*)q; a.k = (const __bf16*)k; a.v = (const __bf16*)v; a.o = (__bf16*)o; a.lse = lse;
+        a.sq_b = strides[0]; a.sq_h = strides[1]; a.sq_t = strides[2];
+        a.sk_b = strides[3]; a.sk_h = strides[4]; a.sk_t = strides[5];
+        a.sv_b = strides[6]; a.sv_h = strides[7]; a.sv_t = strides[8];
+        a.so_b = strides[9]; a.so_h = strides[10]; a.so_t = strides[11];
+        a.B = B; a.H = H; a.scale_log2 = sl2; a.nq = nq; a.nk = nk;
+        return hip_status(vs::launch_attn_bf16(a, head_dim, true, (hipStream_t)stream));
+    }
+    vs::AttnF32Args a{};
+    a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v; a.o = (float*)o; a.lse = lse;
+    a.sq_b = strides[0]; a.sq_h = strides[1]; a.sq_t = strides[2];
+    a.sk_b = strides[3]; a.sk_h = strides[4]; a.sk_t = strides[5];
+    a.sv_b = strides[6]; a.sv_h = strides[7]; a.sv_t = strides[8];
+    a.so_b = strides[9]; a.so_h = strides[10]; a.so_t = strides[11];
+    a.B = B; a.H = H; a.scale_log2 = sl2; a.nq = nq; a.nk = nk;
+    a.g.tile = 8;
+    return hip_status(vs::launch_attn_fp32(a, head_dim, true, (hipStream_t)stream));
+}
+
+const char* varsparse_strerror(int code) {
+    switch (code) {
+        case VARSPARSE_OK: return "ok";
+        case VARSPARSE_EINVAL: return "invalid argument";
+        case VARSPARSE_EUNSUPPORTED: return "unsupported configuration";
+        case VARSPARSE_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+int varsparse_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Kernel argument blocks (passed by value) and launchers of libvarsparse.
+#pragma once
+
+#include "common.h"
+
+namespace vs {
+
+struct AttnArgs {
+    const __bf16* q;
+    const __bf16* k;
+    const __bf16* v;
+    __bf16* o;
+    float* lse;
+    int64_t sq_b, sq_h, sq_t, sk_b, sk_h, sk_t, sv_b, sv_h, sv_t, so_b, so_h, so_t;
+    int32_t B, H;
+    float scale_log2;        // softmax_scale * log2(e)
+    // block-sparse walk
+    const int32_t* kv_cnt;
+    const int32_t* kv_idx;
+    int32_t per_head;
+    int32_t nqb, nkb;
+    int32_t q_side;
+    DevGeom g;
+    // dense walk
+    int64_t nq, nk;
+};
+
+struct AttnF32Args {
+    const float* q;
+    const float* k;
+    const float* v;
+    float* o;
+    float* lse;
+    int64_t sq_b, sq_h, sq_t, sk_b, sk_h, sk_t, sv_b, sv_h, sv_t, so_b, so_h, so_t;
+    int32_t B, H;
+    float scale_log2;
+    const int32_t* kv_cnt;
+    const int32_t* kv_idx;
+    int32_t per_head;
+    int32_t nqb, nkb;
+    int32_t q_side;
+    DevGeom g;
+    int64_t nq, nk;
+};
+
+struct MaskArgs {
+    DevGeom g;
+    int32_t q_scale, n_sink, budget, keep_n, nkb;
+    int32_t radius[kMaxScales];
+    uint8_t* mask;
+    int32_t* kv_cnt;
+    int32_t* kv_idx;
+};
+
+struct ScoreArgs {
+    const __bf16* q;
+    const __bf16* k;
+    float* scores;
+    int64_t sq_b, sq_h, sq_t, sk_b, sk_h, sk_t;
+    int32_t B, H;
+    float scale_log2;
+    int32_t d_side, nqb, nkb;
+    DevGeom g;   // scales 0..D
+};
+
+struct SelMapArgs {
+    DevGeom g;   // scales 0..T
+    int32_t d_scale, t_scale, n_sink, nqbD, nkbD, nqbT, nkbT, words;
+    double top_p;
+    const float* scores;
+    int32_t* sel_cnt;
+    int32_t* sel_idx;
+    int32_t* kv_cnt;
+    int32_t* kv_idx;
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStream_t stream);
+hipError_t launch_attn_fp32(const AttnF32Args& a, int head_dim, bool dense, hipStream_t stream);
+hipError_t launch_csla_mask(const MaskArgs& a, int nqb, hipStream_t stream);
+hipError_t launch_cs4a_score(const ScoreArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_cs4a_select_map(const SelMapArgs& a, int bh, hipStream_t stream);
+
+}  // namespace vs

@@ -1,0 +1,197 @@
+/*
+ * varsparse: block-sparse cross-scale attention for next-scale (VAR) image
+ * generation on AMD Instinct MI355X (gfx950).
+ *
+ * The method is SparVAR's ("SparVAR: Exploring Sparsity in Visual
+ * AutoRegressive Modeling for Training-Free Acceleration"; ai.info summary,
+ * sections "Key Contributions", "Main Findings", "Methodology in Plain
+ * English").  A query scale of the coarse-to-fine generation attends to the
+ * concatenated key/value cache of every earlier scale plus itself.  The keys
+ * a query tile may see are chosen per (query tile, key tile) pair:
+ *   - CSLA: the first scales are attention sinks, visible to every query, and
+ *     elsewhere a key is kept only inside a window around the query's
+ *     projection onto the key's scale; the token mask is aggregated into tiles;
+ *   - CS4A: attention is scored at a mid "decision" scale, the key tiles
+ *     holding most of each query tile's attention mass are selected, and their
+ *     indices are rescaled onto the later, larger scales.
+ * Attention then runs over the kept tiles only.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Scales are 0-based indices into geom->side[] (token-grid sides, strictly
+ * ascending).  A query scale q attends to scales 0..q.  Tiles are square,
+ * geom->tile tokens on a side, partial on the right/bottom edge of a grid
+ * whose side is not a multiple of the tile.  Key tiles are numbered scale by
+ * scale and in raster order within a scale; query tiles in raster order over
+ * the query scale, whose side must be a multiple of the tile.
+ *
+ * Tensors are [B, H, N, head_dim] with the head dimension contiguous: the
+ * caller passes element strides {batch, head, token}.  Q holds the N = side^2
+ * tokens of the query scale in raster order; K and V hold the cache of scales
+ * 0..q, concatenated, each in raster order (Nk = sum of side^2).  bf16 data
+ * and its strides must be 16-byte aligned (strides multiples of 8 elements),
+ * fp32 data 16-byte aligned (strides multiples of 4).
+ *
+ * Kept-tile lists: kv_cnt[r] is the number of kept key tiles of query tile r,
+ * kv_idx[r * nkb + j] for j < kv_cnt[r] their ids in ascending order, the rest
+ * of the row -1.  One list set is either shared by every (b, h) or given per
+ * (b, h), laid out [B][H][nqb] and [B][H][nqb][nkb].
+ *
+ * Memory and errors: every pointer named "dev" is device memory owned by the
+ * caller; the library allocates nothing and keeps no state except a
+ * thread-local copy of the last HIP error.  Arguments are validated on the
+ * host before anything is enqueued; a failed validation enqueues nothing and
+ * returns VARSPARSE_EINVAL (malformed) or VARSPARSE_EUNSUPPORTED (valid but
+ * outside what the kernels implement).  Work is enqueued on `stream` (a
+ * hipStream_t; NULL = the default stream) and is asynchronous; a launch
+ * failure returns VARSPARSE_EHIP.  No C++ exception crosses this interface.
+ */
+#ifndef VARSPARSE_H
+#define VARSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VARSPARSE_MAX_SCALES 32
+
+typedef struct varsparse_geom {
+    int32_t n_scales;                      /* number of scales in side[]            */
+    int32_t side[VARSPARSE_MAX_SCALES];    /* token-grid side of each scale, ascending */
+    int32_t tile;                          /* tile side in tokens                   */
+} varsparse_geom;
+
+typedef enum varsparse_dtype {
+    VARSPARSE_BF16 = 0,  /* bf16 inputs/outputs, fp32 accumulation (MFMA path) */
+    VARSPARSE_FP32 = 1   /* fp32 inputs/outputs and arithmetic                 */
+} varsparse_dtype;
+
+enum {
+    VARSPARSE_OK = 0,
+    VARSPARSE_EINVAL = -1,
+    VARSPARSE_EUNSUPPORTED = -2,
+    VARSPARSE_EHIP = -3
+};
+
+/*
+ * Tile and token counts of query scale q_scale (host only, no HIP call):
+ * nqb query tiles, nkb key tiles of scales 0..q_scale, nq query tokens,
+ * nk cached tokens.  Any output pointer may be NULL.
+ */
+int varsparse_geom_counts(const varsparse_geom* geom, int32_t q_scale,
+                          int32_t* nqb, int32_t* nkb, int64_t* nq, int64_t* nk);
+
+/*
+ * CSLA block mask of query scale q_scale, compacted to kept-tile lists
+ * (SparVAR, ai.info summary, "Methodology in Plain English", second module;
+ * "Main Findings", sink ablation).
+ *
+ * Radius mode (budget == -1): key tile K of scale s is kept for query tile Q
+ * iff s < n_sink, or radius[s] >= 0 and some token pair of Q x K is within
+ * the window: |y' - floor(y h/H)| <= radius[s] and |x' - floor(x h/H)| <=
+ * radius[s], (y, x) a query token at side H, (y', x') a key token at side h.
+ * radius: host array of q_scale + 1 entries, in tokens of each key scale;
+ * a negative entry drops that scale (sinks excepted).
+ *
+ * Budget mode (budget > 0, radius ignored and may be NULL): per query tile
+ * keep the first max(budget, sink tiles + 1) key tiles (at most nkb) ranked by
+ * (not sink, admission radius, -scale, id), the admission radius being the
+ * smallest window radius that keeps the pair.  Supports nkb <= 8192.
+ *
+ * Outputs (dev): mask u8 [nqb * nkb] (1 = kept; may be NULL), kv_cnt int32
+ * [nqb], kv_idx int32 [nqb * nkb] (ascending, -1 padded).  0 <= n_sink <= q_scale.
+ * Bit-exact integer work; the lists are shared by every (batch, head).
+ */
+int varsparse_build_mask(const varsparse_geom* geom, int32_t q_scale, int32_t n_sink,
+                         const int32_t* radius, int32_t budget,
+                         uint8_t* mask, int32_t* kv_cnt, int32_t* kv_idx, void* stream);
+
+/*
+ * CS4A mask prediction (SparVAR, ai.info summary, "Methodology in Plain
+ * English", first module; "Main Findings", decision scale) for target scale
+ * t_scale from decision scale d_scale (d_scale <= t_scale, both sides
+ * multiples of the tile, 0 <= n_sink <= d_scale, 0 < top_p <= 1).
+ *
+ * Scoring (run when q_d != NULL): P = softmax(Q_D K^T * softmax_scale) over
+ * the keys of scales 0..d_scale, per (b, h); scores[b][h][Q][K] =
+ * (1/|Q|) * sum of P over the pairs of query tile Q and key tile K (each row
+ * sums to 1).  q_d: dev [B, H, side_D^2, head_dim] with strides q_strides;
+ * k: dev, the key cache (only its first sum_{s<=D} side^2 tokens are read),
+ * strides k_strides.  bf16 only, head_dim in {64, 128}, tile == 8.
+ * With q_d == NULL, scores are an input (a previous call's output) and k,
+ * q_strides, k_strides, softmax_scale are ignored.
+ * scores: dev float32 [B * H * nqb_D * nkb_D], nkb_D <= 256.
+ *
+ * Selection: per (b, h, decision query tile) the scores are quantised to
+ * m = floor(score * 2^24), ordered by (m descending, id ascending), and the
+ * shortest prefix whose sum reaches ceil(top_p * sum m) (IEEE double) is kept.
+ * sel_cnt int32 [B*H*nqb_D] and sel_idx int32 [B*H*nqb_D*nkb_D] (ascending,
+ * -1 padded) receive it when both are non-NULL.
+ *
+ * Mapping: target query tile (i, j) takes the selection of decision tile
+ * (floor(i nb_D/nb_T), floor(j nb_D/nb_T)); selected tiles of scales below D
+ * are kept; a selected tile of scale D becomes, on every scale s with
+ * D <= s <= t_scale, the tiles covering token rows
+ * [floor(a t h_s/h_D), ceil(e h_s/h_D) - 1] (e the tile's end row) and the
+ * same columns; the sink tiles (scales < n_sink) are added.
+ * kv_cnt int32 [B*H*nqb_T], kv_idx int32 [B*H*nqb_T*nkb_T] (per-(b, h) lists).
+ */
+int varsparse_map_indices(const varsparse_geom* geom, int32_t d_scale, int32_t t_scale,
+                          int32_t n_sink, float top_p, varsparse_dtype dtype,
+                          int32_t B, int32_t H, int32_t head_dim,
+                          const void* q_d, const int64_t q_strides[3],
+                          const void* k, const int64_t k_strides[3], float softmax_scale,
+                          float* scores, int32_t* sel_cnt, int32_t* sel_idx,
+                          int32_t* kv_cnt, int32_t* kv_idx, void* stream);
+
+/*
+ * Block-sparse attention of query scale q_scale over its cache (SparVAR,
+ * ai.info summary, "Key Contributions" item 3 and "Main Findings", the
+ * block-wise sparse kernel).  For every query of tile Q:
+ *     O = softmax(q K_kept^T * softmax_scale) V_kept,
+ *     lse = log(sum over kept keys of exp(q k * softmax_scale)),
+ * K_kept / V_kept the tokens of the kept key tiles of Q.  A query tile with no
+ * kept tile gets O = 0 and lse = -inf.
+ *
+ * q, o: dev [B, H, side_q^2, head_dim]; k, v: dev [B, H, Nk, head_dim];
+ * strides: 12 element strides {q_b, q_h, q_t, k_b, k_h, k_t, v_b, v_h, v_t,
+ * o_b, o_h, o_t}.  lse: dev float32 [B, H, side_q^2] contiguous, or NULL.
+ * kv_cnt / kv_idx: dev lists as above; lists_per_head = 0 for one set shared
+ * by every (b, h), 1 for per-(b, h) lists.  kv_idx entries must be valid,
+ * ascending key-tile ids.
+ * bf16: head_dim in {64, 128}, tile == 8 (64-query tiles).
+ * fp32: head_dim in {64, 128}, tile * tile <= 64.
+ */
+int varsparse_attn_fwd(const varsparse_geom* geom, int32_t q_scale, varsparse_dtype dtype,
+                       int32_t B, int32_t H, int32_t head_dim,
+                       const void* q, const void* k, const void* v, void* o, float* lse,
+                       const int64_t strides[12], float softmax_scale,
+                       const int32_t* kv_cnt, const int32_t* kv_idx, int32_t lists_per_head,
+                       void* stream);
+
+/*
+ * Dense attention written with the same tile engine, the comparator the
+ * pages measure the sparse kernel against ("Main Findings": the block-wise
+ * kernel vs dense FlashAttention on the last scale).  Every query attends to
+ * all nk keys.  Layouts and lse as for varsparse_attn_fwd; nq, nk >= 1.
+ * bf16 or fp32, head_dim in {64, 128}.
+ */
+int varsparse_dense_attn_fwd(varsparse_dtype dtype, int32_t B, int32_t H, int32_t head_dim,
+                             int64_t nq, int64_t nk,
+                             const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int64_t strides[12], float softmax_scale, void* stream);
+
+/* Static description of a status code. */
+const char* varsparse_strerror(int code);
+
+/* The hipError_t of the calling thread's last VARSPARSE_EHIP (0 if none). */
+int varsparse_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VARSPARSE_H */

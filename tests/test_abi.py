@@ -1,0 +1,135 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, computes counts on the host, and rejects malformed or
+unsupported arguments before touching HIP (every call here fails validation,
+so none of them launches anything)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+vs = pytest.importorskip("block_sparse_cross_csla_amd")
+from block_sparse_cross_csla_amd import _lib  # noqa: E402
+from varsparse_inputs import SCHEDULE_13, SCHEDULE_16, TINY_SIDES  # noqa: E402
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "varsparse.h")
+
+
+def test_exports_every_declared_function():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(varsparse_\w+)\s*\(", text, re.M))
+    assert declared == set(_lib.EXPORTS)
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_geom_counts():
+    assert vs.geom_counts(SCHEDULE_13, 8, 12) == (64, 172, 4096, 10521)
+    assert vs.geom_counts(SCHEDULE_13, 8, 9) == (16, 47, 1024, 2521)
+    assert vs.geom_counts(TINY_SIDES, 4, 4) == (16, 23, 256, 341)
+    assert vs.geom_counts(SCHEDULE_16, 8, 15) == (256, 672, 16384, 42521)
+
+
+def test_strerror():
+    lib = _lib.lib()
+    for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-2, b"unsupported configuration"),
+                       (-3, b"HIP launch error")]:
+        assert lib.varsparse_strerror(code) == text
+    assert lib.varsparse_last_hip_error() == 0
+
+
+def _g(sides=SCHEDULE_13, tile=8):
+    return ctypes.byref(_lib.make_geom(sides, tile))
+
+
+FAKE = ctypes.c_void_p(1 << 20)       # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p((1 << 20) + 2)
+I32 = ctypes.c_int32
+
+
+def _strides(vals):
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+GOOD12 = [0, 0, 128] * 4
+
+
+@pytest.mark.parametrize("sides,tile", [((), 8), ((4, 4), 8), ((4, 2), 8), ((0, 4), 8), ((2, 4), 0)])
+def test_bad_geometry(sides, tile):
+    lib = _lib.lib()
+    assert lib.varsparse_geom_counts(_g(sides, tile), 0, None, None, None, None) == _lib.EINVAL
+
+
+def test_build_mask_validation():
+    lib = _lib.lib()
+    rad = (I32 * 13)(*([2] * 13))
+    call = lambda **kw: lib.varsparse_build_mask(  # noqa: E731
+        kw.get("g", _g()), kw.get("q", 12), kw.get("n_sink", 5), kw.get("rad", rad), kw.get("budget", -1),
+        None, kw.get("cnt", FAKE), kw.get("idx", FAKE), None)
+    assert call(q=13) == _lib.EINVAL                      # query scale out of range
+    assert call(q=-1) == _lib.EINVAL
+    assert call(n_sink=13) == _lib.EINVAL                 # more sinks than earlier scales
+    assert call(n_sink=-1) == _lib.EINVAL
+    assert call(budget=0) == _lib.EINVAL
+    assert call(budget=-2) == _lib.EINVAL
+    assert call(rad=None) == _lib.EINVAL                  # radius mode needs radii
+    assert call(cnt=None) == _lib.EINVAL
+    assert call(idx=None) == _lib.EINVAL
+    assert call(g=_g(SCHEDULE_13, 7)) == _lib.EINVAL      # side 64 not a multiple of the tile
+
+
+def test_attn_validation():
+    lib = _lib.lib()
+
+    def call(**kw):
+        return lib.varsparse_attn_fwd(
+            kw.get("g", _g()), kw.get("q", 12), kw.get("dt", _lib.BF16), kw.get("B", 2), kw.get("H", 16),
+            kw.get("d", 128), kw.get("qp", FAKE), FAKE, FAKE, FAKE, None, _strides(kw.get("st", GOOD12)),
+            kw.get("scale", 0.088), FAKE, FAKE, kw.get("per_head", 0), None)
+    assert call(d=96) == _lib.EUNSUPPORTED
+    assert call(d=256) == _lib.EUNSUPPORTED
+    assert call(g=_g(SCHEDULE_13, 4)) == _lib.EUNSUPPORTED    # bf16 MFMA path uses 8x8 tiles
+    assert call(g=_g(TINY_SIDES, 16), q=4, dt=_lib.FP32, d=64) == _lib.EUNSUPPORTED
+    assert call(dt=7) == _lib.EINVAL
+    assert call(B=0) == _lib.EINVAL
+    assert call(scale=0.0) == _lib.EINVAL
+    assert call(scale=float("nan")) == _lib.EINVAL
+    assert call(qp=None) == _lib.EINVAL
+    assert call(qp=MISALIGNED) == _lib.EINVAL
+    assert call(st=[0, 0, 132] + GOOD12[3:]) == _lib.EINVAL   # bf16 rows not 16-byte aligned
+    assert call(per_head=2) == _lib.EINVAL
+    assert call(q=13) == _lib.EINVAL
+
+
+def test_dense_validation():
+    lib = _lib.lib()
+
+    def call(**kw):
+        return lib.varsparse_dense_attn_fwd(kw.get("dt", _lib.BF16), 1, 1, kw.get("d", 128), kw.get("nq", 10),
+                                            kw.get("nk", 10), FAKE, FAKE, FAKE, FAKE, None,
+                                            _strides(GOOD12), kw.get("scale", 0.1), None)
+    assert call(nq=0) == _lib.EINVAL
+    assert call(nk=0) == _lib.EINVAL
+    assert call(d=32) == _lib.EUNSUPPORTED
+    assert call(scale=-1.0) == _lib.EINVAL
+    assert call(nk=1 << 31) == _lib.EUNSUPPORTED
+
+
+def test_map_indices_validation():
+    lib = _lib.lib()
+
+    def call(**kw):
+        return lib.varsparse_map_indices(
+            _g(), kw.get("D", 9), kw.get("T", 12), kw.get("n_sink", 5), kw.get("p", 0.9), _lib.BF16, 2, 16,
+            kw.get("d", 128), kw.get("qd", None), None, None, None, 0.1, kw.get("scores", FAKE),
+            kw.get("sel_cnt", None), None, FAKE, FAKE, None)
+    assert call(D=13) == _lib.EINVAL
+    assert call(D=10, T=9) == _lib.EINVAL
+    assert call(n_sink=10) == _lib.EINVAL
+    assert call(p=0.0) == _lib.EINVAL
+    assert call(p=1.5) == _lib.EINVAL
+    assert call(scores=None) == _lib.EINVAL
+    assert call(sel_cnt=FAKE) == _lib.EINVAL             # selection outputs come in pairs
+    assert call(qd=FAKE) == _lib.EINVAL                  # scoring needs k and strides
+    assert call(qd=FAKE, d=96) == _lib.EUNSUPPORTED

@@ -1,0 +1,201 @@
+"""GPU parity: block-sparse and dense attention against the oracle.
+
+Tolerances: bf16 outputs within max-abs 2e-2 of the float64 oracle on the
+same bf16 inputs; fp32 outputs within 1e-4; lse alike."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as OA, geometry as G
+from tests._common import gaussian, lists, oracle_mask, spatial, to_device
+from varsparse_inputs import SCHEDULE_13, workloads as W
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+FP32_TOL = 1e-4
+
+
+def _vs():
+    import block_sparse_cross_csla_amd as vs
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return vs
+
+
+def _compare(o_gpu, lse_gpu, o_ref, lse_ref, tol, where=""):
+    o = o_gpu.float().cpu().numpy().astype(np.float64)
+    sel = ~np.isnan(o_ref[..., 0])
+    err = np.abs(o - o_ref)[sel].max()
+    assert err <= tol, f"{where} max |O - O_ref| = {err}"
+    if lse_gpu is not None:
+        lg = lse_gpu.cpu().numpy().astype(np.float64)
+        fin = np.isfinite(lse_ref) & sel
+        assert (np.isneginf(lg[~np.isfinite(lse_ref) & sel])).all()
+        if fin.any():
+            e2 = np.abs(lg[fin] - lse_ref[fin]).max()
+            assert e2 <= tol, f"{where} max |lse - lse_ref| = {e2}"
+    return err
+
+
+def test_fp32_tiny_workload():
+    vs = _vs()
+    w = W.TINY
+    nqb, nkb, nq, nk = G.counts(w.sides, w.q_scale, w.tile)
+    q, k, v = gaussian(w.seed, w.wid, w.B, w.H, nq, nk, w.d, bf16=False)
+    cnt, idx, _ = vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, radius=w.radii)
+    o, lse = vs.attn_fwd(to_device(q, torch.float32), to_device(k, torch.float32), to_device(v, torch.float32),
+                         w.sides, w.tile, w.q_scale, cnt, idx, softmax_scale=1 / math.sqrt(w.d))
+    torch.cuda.synchronize()
+    mc, mi = lists(oracle_mask(tuple(w.sides), w.q_scale, w.tile, w.n_sink, tuple(w.radii)))
+    ro, rl = OA.block_sparse_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                       w.sides, w.q_scale, w.tile, mc, mi, 1 / math.sqrt(w.d))
+    _compare(o, lse, ro, rl, FP32_TOL, "tiny fp32")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_bf16_last_scale_every_tile(d):
+    """The 2B-shaped last scale (side 64 over 10521 cached tokens), one batch
+    and two heads, every query tile compared."""
+    vs = _vs()
+    w = W.LAST_SCALE_2B
+    q, k, v = spatial(w, B=1, H=2)
+    if d != w.d:
+        q, k, v = q[..., :d].copy(), k[..., :d].copy(), v[..., :d].copy()
+    cnt, idx, _ = vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, radius=w.radii)
+    o, lse = vs.attn_fwd(to_device(q), to_device(k), to_device(v), w.sides, w.tile, w.q_scale, cnt, idx)
+    torch.cuda.synchronize()
+    mc, mi = lists(oracle_mask(tuple(w.sides), w.q_scale, w.tile, w.n_sink, tuple(w.radii)))
+    ro, rl = OA.block_sparse_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                       w.sides, w.q_scale, w.tile, mc, mi, 1 / math.sqrt(d))
+    _compare(o, lse, ro, rl, BF16_TOL, f"last scale d={d}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_bf16_partial_tiles(d):
+    """Scales whose sides are not multiples of the tile (3, 5, 12, 20) give
+    partial key tiles; side 40 queries (5 x 5 tiles)."""
+    vs = _vs()
+    sides = (1, 2, 3, 5, 8, 12, 20, 24, 40)
+    qs, t = 8, 8
+    nqb, nkb, nq, nk = G.counts(sides, qs, t)
+    q, k, v = gaussian(3, 31, 1, 2, nq, nk, d)
+    radius = (2,) * 9
+    cnt, idx, _ = vs.build_mask(sides, t, qs, 2, radius=radius)
+    o, lse = vs.attn_fwd(to_device(q), to_device(k), to_device(v), sides, t, qs, cnt, idx)
+    torch.cuda.synchronize()
+    mc, mi = lists(oracle_mask(sides, qs, t, 2, radius))
+    ro, rl = OA.block_sparse_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                       sides, qs, t, mc, mi, 1 / math.sqrt(d))
+    _compare(o, lse, ro, rl, BF16_TOL, f"partial tiles d={d}")
+
+
+def test_bf16_per_head_lists_empty_rows_and_dense_rows():
+    """Per-(b,h) lists drawn at random: rows with no tile (O = 0, lse = -inf),
+    rows with every tile, rows that do not start at tile 0, and rows longer
+    than 64 entries (the list is read in windows of 64)."""
+    vs = _vs()
+    sides, qs, t = SCHEDULE_13, 11, 8
+    B, H, d = 2, 2, 128
+    nqb, nkb, nq, nk = G.counts(sides, qs, t)
+    rng = np.random.default_rng(11)
+    keep = rng.random((B, H, nqb, nkb)) < rng.choice([0.05, 0.3, 0.7], size=(B, H, nqb, 1))
+    keep[0, 0, 0] = False
+    keep[0, 1, 1] = True
+    keep[1, 0, 2] = False
+    keep[1, 0, 2, 5:9] = True
+    keep[1, 1, :, :3] = True
+    cnt, idx = lists(keep)
+    q, k, v = gaussian(4, 41, B, H, nq, nk, d)
+    o, lse = vs.attn_fwd(to_device(q), to_device(k), to_device(v), sides, t, qs,
+                         torch.from_numpy(cnt).cuda(), torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    ro, rl = OA.block_sparse_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                       sides, qs, t, cnt, idx, 1 / math.sqrt(d))
+    _compare(o, lse, ro, rl, BF16_TOL, "per-head lists")
+    o0 = o[0, 0, G.query_tiles(sides, qs, t)[0].tokens()].float()
+    assert (o0 == 0).all()
+    assert torch.isneginf(lse[0, 0, G.query_tiles(sides, qs, t)[0].tokens()]).all()
+
+
+@pytest.mark.parametrize("nq,nk,d", [(300, 1000, 128), (64, 32, 128), (1, 1, 128), (130, 257, 64), (2304, 6425, 128)])
+def test_bf16_dense(nq, nk, d):
+    vs = _vs()
+    q, k, v = gaussian(5, 51, 1, 2, nq, nk, d)
+    o, lse = vs.dense_attn_fwd(to_device(q), to_device(k), to_device(v))
+    torch.cuda.synchronize()
+    ro, rl = OA.dense_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), 1 / math.sqrt(d))
+    _compare(o, lse, ro, rl, BF16_TOL, f"dense {nq}x{nk} d={d}")
+
+
+@pytest.mark.parametrize("nq,nk,d", [(100, 333, 64), (64, 64, 128)])
+def test_fp32_dense(nq, nk, d):
+    vs = _vs()
+    q, k, v = gaussian(6, 61, 1, 2, nq, nk, d, bf16=False)
+    o, lse = vs.dense_attn_fwd(to_device(q, torch.float32), to_device(k, torch.float32), to_device(v, torch.float32))
+    torch.cuda.synchronize()
+    ro, rl = OA.dense_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), 1 / math.sqrt(d))
+    _compare(o, lse, ro, rl, FP32_TOL, f"fp32 dense {nq}x{nk}")
+
+
+def test_non_contiguous_strides():
+    """Q/K/V/O as views of larger buffers (token stride > head dim)."""
+    vs = _vs()
+    w = W.LAST_SCALE_2B
+    sides, qs, t = w.sides[:10], 9, 8
+    nqb, nkb, nq, nk = G.counts(sides, qs, t)
+    q, k, v = gaussian(7, 71, 1, 2, nq, nk, 128)
+    big = lambda x: torch.cat([to_device(x), to_device(np.zeros_like(x))], dim=-1)[..., :128]  # noqa: E731
+    qd, kd, vd = big(q), big(k), big(v)
+    out = torch.zeros(1, 2, nq, 256, dtype=torch.bfloat16, device="cuda")[..., 64:192]
+    cnt, idx, _ = vs.build_mask(sides, t, qs, 5, radius=(2,) * 10)
+    o, lse = vs.attn_fwd(qd, kd, vd, sides, t, qs, cnt, idx, out=out)
+    torch.cuda.synchronize()
+    mc, mi = lists(oracle_mask(tuple(sides), qs, t, 5, (2,) * 10))
+    ro, rl = OA.block_sparse_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                       sides, qs, t, mc, mi, 1 / math.sqrt(128))
+    _compare(o, lse, ro, rl, BF16_TOL, "strided")
+
+
+SAMPLE_TILES = [0, 7, 9, 27, 36, 56, 63]
+
+
+def test_full_size_2b_last_scale_sampled_and_deterministic():
+    """The benchmarked launch: B=2, H=16, d=128, side 64 over 10521 tokens."""
+    vs = _vs()
+    w = W.LAST_SCALE_2B
+    q, k, v = spatial(w)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    cnt, idx, _ = vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, radius=w.radii)
+    o1, l1 = vs.attn_fwd(qd, kd, vd, w.sides, w.tile, w.q_scale, cnt, idx)
+    o2, l2 = vs.attn_fwd(qd, kd, vd, w.sides, w.tile, w.q_scale, cnt, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    mc, mi = lists(oracle_mask(tuple(w.sides), w.q_scale, w.tile, w.n_sink, tuple(w.radii)))
+    bh = [(0, 0), (1, 15), (0, 7), (1, 3)]
+    ro, rl = OA.block_sparse_attention(q, k, v, w.sides, w.q_scale, w.tile, mc, mi, 1 / math.sqrt(w.d),
+                                       q_tiles=SAMPLE_TILES, bh=bh)
+    _compare(o1, l1, ro, rl, BF16_TOL, "2B full size")
+    # dense comparator on the same tensors, a few query rows
+    od, ld = vs.dense_attn_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 64, 2047, 4095]
+    rdo, rdl = OA.dense_attention(q, k, v, 1 / math.sqrt(w.d), q_rows=rows, bh=bh)
+    _compare(od, ld, rdo, rdl, BF16_TOL, "2B dense full size")
+
+
+def test_full_size_high_res_sampled():
+    """High-resolution stress: B=1, H=16, side 128 queries over 42521 tokens."""
+    vs = _vs()
+    w = W.HIGH_RES
+    q, k, v = spatial(w)
+    cnt, idx, _ = vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, radius=w.radii)
+    o, lse = vs.attn_fwd(to_device(q), to_device(k), to_device(v), w.sides, w.tile, w.q_scale, cnt, idx)
+    torch.cuda.synchronize()
+    mask = oracle_mask(tuple(w.sides), w.q_scale, w.tile, w.n_sink, tuple(w.radii))
+    assert (cnt.cpu().numpy() == mask.sum(1)).all()
+    mc, mi = lists(mask)
+    ro, rl = OA.block_sparse_attention(q, k, v, w.sides, w.q_scale, w.tile, mc, mi, 1 / math.sqrt(w.d),
+                                       q_tiles=[0, 15, 100, 137, 255], bh=[(0, 0), (0, 9), (0, 15)])
+    _compare(o, lse, ro, rl, BF16_TOL, "high-res")
