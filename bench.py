@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cs4a", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -173,6 +175,13 @@ def main():
                      "traffic": None, "kernel": "attn_fwd_bf16_kernel<128,false>",
                      "flop_per_launch": flops},
     }
+
+    if args.copy_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     if not args.no_cs4a:
         result["cs4a"] = bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev)

@@ -42,6 +42,12 @@ bool strides_ok(const int64_t* st, int n, int64_t unit) {
 
 bool scale_ok(float s) { return isfinite(s) && s > 0.0f; }
 
+// The bf16 kernels address K and V of one head with 32-bit byte offsets.
+bool offsets_fit(int64_t nk, int64_t sk_t, int64_t sv_t, int head_dim) {
+    const int64_t lim = (int64_t)1 << 31;
+    return (nk - 1) * sk_t * 2 + head_dim * 2 < lim && (nk - 1) * sv_t * 2 + head_dim * 2 < lim;
+}
+
 constexpr double kLog2e = 1.4426950408889634;
 
 }  // namespace
@@ -177,6 +183,7 @@ int varsparse_attn_fwd(const varsparse_geom* geom, int32_t q_scale, varsparse_dt
     if ((int64_t)nqb * B * H > 0x7fffffff) return VARSPARSE_EINVAL;
     const float sl2 = (float)(softmax_scale * kLog2e);
     if (dtype == VARSPARSE_BF16) {
+        if (!offsets_fit(g.tok_off[q_scale + 1], strides[5], strides[8], head_dim)) return VARSPARSE_EUNSUPPORTED;
         vs::AttnArgs a{};
         a.q = (const __bf16*)q; a.k = (const __bf16*)k; a.v = (const __bf16*)v; a.o = (__bf16*)o; a.lse = lse;
         a.sq_b = strides[0]; a.sq_h = strides[1]; a.sq_t = strides[2];
@@ -214,6 +221,7 @@ int varsparse_dense_attn_fwd(varsparse_dtype dtype, int32_t B, int32_t H, int32_
     if (((nq + 63) / 64) * B * H > 0x7fffffff) return VARSPARSE_EINVAL;
     const float sl2 = (float)(softmax_scale * kLog2e);
     if (dtype == VARSPARSE_BF16) {
+        if (!offsets_fit(nk, strides[5], strides[8], head_dim)) return VARSPARSE_EUNSUPPORTED;
         vs::AttnArgs a{};
         a.q = (const __bf16*)q; a.k = (const __bf16*)k; a.v = (const __bf16*)v; a.o = (__bf16*)o; a.lse = lse;
         a.sq_b = strides[0]; a.sq_h = strides[1]; a.sq_t = strides[2];

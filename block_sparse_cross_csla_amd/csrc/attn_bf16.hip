@@ -13,12 +13,16 @@
 //    tokens), or 32 consecutive tokens of the leading run of wholly kept
 //    scales (the sink scales are contiguous in the cache, so their small tiles
 //    are packed instead of padded);
+//  * the kept-tile list is decoded 64 entries at a time, one entry per lane
+//    (token base, row stride, rows, cols), and read back per chunk with
+//    readlane, so the walk itself costs a few scalar instructions per chunk;
 //  * K and V chunks go HBM -> LDS with gfx950's 16-byte-per-lane direct loads
-//    (global_load_lds_dwordx4), double buffered, rows XOR-swizzled in 16-byte
+//    (global_load_lds_dwordx4, 64-bit head base in SGPRs, 32-bit lane offset:
+//    one VALU add per load), double buffered, rows XOR-swizzled in 16-byte
 //    units so that the MFMA operand reads below are bank-conflict free;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in
 //    registers for the whole walk), so that every lane holds the scores of a
-//    single query: row max needs one cross-lane exchange, row sums none;
+//    single query: the row max needs one v_permlane32_swap, row sums none;
 //  * online softmax in the exp2 domain; the running max is only raised when a
 //    new score exceeds it by more than 2^8 in the exponent (exact in
 //    arithmetic: the final normalisation uses the same stale max);
@@ -35,22 +39,43 @@ struct Chunk {
     int32_t base, stride, nrows, ncols, nvalid;
 };
 
-// Walk state over the kept keys of one query tile.  The tile list is read 64
-// entries at a time into one register (lane i holds entry cache_base + i) and
-// entries are broadcast with readlane, so the walk issues no scalar or vector
-// loads between refills.
+// Walk state over the kept keys of one query tile.  Lane i of desc0/desc1
+// holds the decoded list entry cache_base + i: token base of the tile, and
+// stride | rows << 16 | cols << 24.
 struct Cursor {
     int32_t cnext, cend;   // leading contiguous token run [cnext, cend)
     int32_t j, cnt;        // position in the kept-tile list
     int32_t half;          // which half (rows 0-3 / 4-7) of tile j comes next
     const int32_t* idx;
     int32_t cache_base;
-    int32_t cache;
+    int32_t desc0, desc1;
 };
 
-__device__ __forceinline__ void cursor_fill(Cursor& c, int lane) {
+// Decode list entries cache_base .. cache_base+63 (one per lane).  Entries are
+// documented to be valid tile ids; out-of-range ids are clamped so that a bad
+// list cannot address outside the cache.
+__device__ __forceinline__ void cursor_fill(Cursor& c, const DevGeom& g, int lane) {
     c.cache_base = c.j;
-    c.cache = (c.j + lane < c.cnt) ? c.idx[c.j + lane] : 0;
+    const int e = c.j + lane;
+    int id = e < c.cnt ? c.idx[e] : 0;
+    id = min(max(id, 0), g.tile_base[g.n_scales] - 1);
+    int tb = 0, side = g.side[0], off = 0, nb = g.nb[0];
+    for (int s = 1; s < g.n_scales; ++s) {
+        if (id >= g.tile_base[s]) {
+            tb = g.tile_base[s];
+            side = g.side[s];
+            off = g.tok_off[s];
+            nb = g.nb[s];
+        }
+    }
+    const int local = id - tb;
+    int a = (int)(((float)local + 0.5f) / (float)nb);
+    a -= (a * nb > local);
+    a += ((a + 1) * nb <= local);
+    const int b = local - a * nb, t = g.tile;
+    const int rows = min(t, side - a * t), cols = min(t, side - b * t);
+    c.desc0 = off + a * t * side + b * t;
+    c.desc1 = side | (rows << 16) | (cols << 24);
 }
 
 __device__ __forceinline__ bool cursor_next(Cursor& c, const DevGeom& g, Chunk& out, int lane) {
@@ -64,18 +89,13 @@ __device__ __forceinline__ bool cursor_next(Cursor& c, const DevGeom& g, Chunk& 
         return true;
     }
     if (c.j >= c.cnt) return false;
-    if (c.j - c.cache_base >= 64) cursor_fill(c, lane);
-    // entries are documented to be valid tile ids; clamp anyway so that a bad
-    // list cannot address outside the cache
-    const int id = min(max(__builtin_amdgcn_readlane(c.cache, c.j - c.cache_base), 0),
-                       g.tile_base[g.n_scales] - 1);
-    const int s = scale_of_tile(g, id);
-    const int local = id - g.tile_base[s];
-    const int nb = g.nb[s], side = g.side[s], t = g.tile;
-    const int a = local / nb, b = local - a * nb;
-    const int rows = min(t, side - a * t), cols = min(t, side - b * t);
+    if (c.j - c.cache_base >= 64) cursor_fill(c, g, lane);
+    const int slot = c.j - c.cache_base;
+    const int base = __builtin_amdgcn_readlane(c.desc0, slot);
+    const int info = __builtin_amdgcn_readlane(c.desc1, slot);
+    const int side = info & 0xffff, rows = (info >> 16) & 0xff, cols = info >> 24;
     const int r0 = 4 * c.half;
-    out.base = g.tok_off[s] + (a * t + r0) * side + b * t;
+    out.base = base + r0 * side;
     out.stride = side;
     out.nrows = min(4, rows - r0);
     out.ncols = cols;
@@ -89,24 +109,58 @@ __device__ __forceinline__ bool cursor_next(Cursor& c, const DevGeom& g, Chunk& 
     return true;
 }
 
+// Per-lane constants of the chunk loads.  A wave fills key rows
+// [16 wave, 16 wave + 16) of a stage; load i covers RPL consecutive rows, whose
+// chunk row (key slot / 8) is the same for the whole wave.
 template <int D>
-__device__ __forceinline__ void load_chunk(const __bf16* __restrict__ kh, const __bf16* __restrict__ vh,
-                                           int64_t sk_t, int64_t sv_t, const Chunk& c,
-                                           uint32_t k_lds, uint32_t v_lds, int wave, int lane) {
-    constexpr int ROWB = D * 2;           // bytes per key row
-    constexpr int CH = D / 8;             // 16-byte units per row
-    constexpr int RPL = 1024 / ROWB;      // key rows filled by one wave-wide load
-    constexpr int LOADS = 16 / RPL;       // loads per wave per tensor (a wave fills 16 rows)
+struct LoadPlan {
+    static constexpr int ROWB = D * 2;          // LDS bytes per key row
+    static constexpr int CH = D / 8;            // 16-byte units per row
+    static constexpr int RPL = 1024 / ROWB;     // rows per wave-wide load
+    static constexpr int LOADS = 16 / RPL;      // loads per wave per tensor
+    int32_t kc[LOADS], vc[LOADS];   // col * row_bytes + unit offset (K, V)
+    int32_t lu[LOADS];              // unit offset alone (clamped slots)
+    int32_t col[LOADS];             // token column within the chunk row
+    int32_t slot[LOADS];            // key slot 0..31
+};
+
+template <int D>
+__device__ __forceinline__ void make_plan(LoadPlan<D>& p, int wave, int lane, int64_t sk_t, int64_t sv_t) {
+    using P = LoadPlan<D>;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int row = 16 * wave + i * RPL + lane / CH;
-        const int lc = (lane % CH) ^ swz<CH>(row);
-        const int r = row >> 3, col = row & 7;
-        const bool valid = r < c.nrows && col < c.ncols && row < c.nvalid;
-        const int tok = valid ? c.base + r * c.stride + col : c.base;
-        const uint32_t off = (uint32_t)((16 * wave + i * RPL) * ROWB);
-        lds_dma16(kh + tok * sk_t + lc * 8, __builtin_amdgcn_readfirstlane(k_lds + off));
-        lds_dma16(vh + tok * sv_t + lc * 8, __builtin_amdgcn_readfirstlane(v_lds + off));
+    for (int i = 0; i < P::LOADS; ++i) {
+        const int row = 16 * wave + i * P::RPL + lane / P::CH;
+        const int unit = (lane % P::CH) ^ swz<P::CH>(row);
+        p.slot[i] = row;
+        p.col[i] = row & 7;
+        p.lu[i] = unit * 16;
+        p.kc[i] = (row & 7) * (int32_t)(sk_t * 2) + unit * 16;
+        p.vc[i] = (row & 7) * (int32_t)(sv_t * 2) + unit * 16;
+        // opaque to the optimizer: keeps the per-chunk address at one add
+        // instead of a re-associated per-lane multiply
+        asm volatile("" : "+v"(p.kc[i]), "+v"(p.vc[i]), "+v"(p.lu[i]));
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void load_chunk(const LoadPlan<D>& p, const __bf16* kh, const __bf16* vh, int32_t krb,
+                                           int32_t vrb, const Chunk& c, uint32_t k_lds, uint32_t v_lds,
+                                           int wave) {
+    using P = LoadPlan<D>;
+    const bool full = c.nrows == 4 && c.ncols == 8 && c.nvalid == 32;
+#pragma unroll
+    for (int i = 0; i < P::LOADS; ++i) {
+        const int r = (16 * wave + i * P::RPL) >> 3;     // chunk row of this load (wave-uniform)
+        const int32_t ks = (c.base + r * c.stride) * krb, vs_ = (c.base + r * c.stride) * vrb;
+        int32_t ko = ks + p.kc[i], vo = vs_ + p.vc[i];
+        if (!full) {
+            const bool valid = r < c.nrows && p.col[i] < c.ncols && p.slot[i] < c.nvalid;
+            ko = valid ? ko : c.base * krb + p.lu[i];
+            vo = valid ? vo : c.base * vrb + p.lu[i];
+        }
+        const uint32_t dst = (uint32_t)((16 * wave + i * P::RPL) * P::ROWB);
+        lds_dma16_off(kh, ko, __builtin_amdgcn_readfirstlane(k_lds + dst));
+        lds_dma16_off(vh, vo, __builtin_amdgcn_readfirstlane(v_lds + dst));
     }
 }
 
@@ -117,6 +171,16 @@ struct WaveState {
     f32x16 oacc[D / 32];          // O^T accumulator
     float m_run, l_run;           // running max (log2 domain) and this lane's partial sum
 };
+
+// max / sum of a value and its partner lane (lane ^ 32) via v_permlane32_swap
+__device__ __forceinline__ float half_swap_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Consume one chunk of 32 keys from LDS (kst: K rows, vst: V rows).
 template <int D>
@@ -149,7 +213,7 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
     float mx = sacc[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = half_swap_max(mx);
     const float cand = mx * c;
     const bool need = cand > st.m_run + kLazy;
     if (__ballot(need)) {
@@ -190,22 +254,15 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
     }
 }
 
-// LDS stages: one array per (buffer, tensor) so that alias analysis can tell a
-// stage being read from the stage being filled by the LDS-DMA prefetch.
-template <int D>
-struct Stages {
-    static constexpr int BYTES = 32 * D * 2;
-};
-
 template <int D, bool DENSE>
 __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a) {
     constexpr int KSTEPS = D / 16;
     constexpr int MBLK = D / 32;
-    constexpr int STAGE = Stages<D>::BYTES;
-    constexpr int LOADS = 2 * (16 / (1024 / (D * 2)));   // vm instructions per wave per chunk
+    constexpr int STAGE = 32 * D * 2;
+    constexpr int LOADS = 2 * LoadPlan<D>::LOADS;   // vm instructions per wave per chunk
     __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];   // [stage][K, V]
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n = lane & 31, g = lane >> 5;  // query column and lane half of this lane
 
     const int64_t nqt = DENSE ? (a.nq + 63) / 64 : a.nqb;
@@ -235,6 +292,9 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     st.l_run = 0.0f;
     const __bf16* kh = a.k + b * a.sk_b + h * a.sk_h;
     const __bf16* vh = a.v + b * a.sv_b + h * a.sv_h;
+    const int32_t krb = (int32_t)(a.sk_t * 2), vrb = (int32_t)(a.sv_t * 2);
+    LoadPlan<D> plan;
+    make_plan<D>(plan, wave, lane, a.sk_t, a.sv_t);
 
     // ---- kept-key walk
     Cursor cur;
@@ -245,7 +305,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         cur.j = cur.cnt = 0;
         cur.idx = nullptr;
         cur.cache_base = 0;
-        cur.cache = 0;
+        cur.desc0 = cur.desc1 = 0;
     } else {
         const int64_t row = (a.per_head ? (int64_t)bh * a.nqb : 0) + qt;
         cur.cnt = a.kv_cnt[row];
@@ -267,7 +327,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         cur.cnext = 0;
         cur.cend = a.g.tok_off[s];
         cur.j = a.g.tile_base[s];
-        cursor_fill(cur, lane);
+        cursor_fill(cur, a.g, lane);
     }
     wait_vmcnt(0);   // Q and the first list entries are in registers before LDS-DMA traffic starts
     const float c = a.scale_log2;
@@ -276,12 +336,12 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     const char* sm = smem;
     Chunk cc, cn;
     bool have = cursor_next(cur, a.g, cc, lane);
-    if (have) load_chunk<D>(kh, vh, a.sk_t, a.sv_t, cc, lds0, lds0 + STAGE, wave, lane);
+    if (have) load_chunk<D>(plan, kh, vh, krb, vrb, cc, lds0, lds0 + STAGE, wave);
     while (have) {
         // stage 0 holds chunk cc; prefetch the next one into stage 1
         bool more = cursor_next(cur, a.g, cn, lane);
         if (more) {
-            load_chunk<D>(kh, vh, a.sk_t, a.sv_t, cn, lds0 + 2 * STAGE, lds0 + 3 * STAGE, wave, lane);
+            load_chunk<D>(plan, kh, vh, krb, vrb, cn, lds0 + 2 * STAGE, lds0 + 3 * STAGE, wave);
             wait_vmcnt(LOADS);
         } else {
             wait_vmcnt(0);
@@ -294,7 +354,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         // stage 1 holds chunk cc; prefetch the next one into stage 0
         more = cursor_next(cur, a.g, cn, lane);
         if (more) {
-            load_chunk<D>(kh, vh, a.sk_t, a.sv_t, cn, lds0, lds0 + STAGE, wave, lane);
+            load_chunk<D>(plan, kh, vh, krb, vrb, cn, lds0, lds0 + STAGE, wave);
             wait_vmcnt(LOADS);
         } else {
             wait_vmcnt(0);
@@ -307,7 +367,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     }
 
     // ---- epilogue
-    const float l_tot = st.l_run + __shfl_xor(st.l_run, 32);
+    const float l_tot = half_swap_sum(st.l_run);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if (qvalid) {
         __bf16* op = a.o + b * a.so_b + h * a.so_h + tok * a.so_t;

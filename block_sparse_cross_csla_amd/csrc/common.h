@@ -96,6 +96,13 @@ __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds) {
                  :: "v"(gaddr), "s"(lds) : "memory", "m0");
 }
 
+// Same, addressed as a wave-uniform 64-bit base (SGPR pair) plus a per-lane
+// 32-bit byte offset: no 64-bit address arithmetic in VGPRs.
+__device__ __forceinline__ void lds_dma16_off(const void* base, int32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)p);
 }

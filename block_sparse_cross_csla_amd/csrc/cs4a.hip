@@ -33,7 +33,7 @@ __global__ __launch_bounds__(128) void cs4a_score_kernel(const ScoreArgs a) {
     char* kst_base = dyn;                              // [2][STAGE]
     float* acc = (float*)(dyn + 2 * STAGE);            // [nkb][128]
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n = lane & 31, g = lane >> 5;
     const int bh = blockIdx.x / a.nqb, qt = blockIdx.x - bh * a.nqb;
     const int b = bh / a.H, h = bh - b * a.H;
