@@ -35,78 +35,89 @@ namespace vs {
 
 // One chunk of up to 32 keys: key slot k (0..31) is token
 // base + (k/8)*stride + (k%8), valid iff k/8 < nrows, k%8 < ncols, k < nvalid.
+// Packed as two words: base, and stride | nrows << 16 | ncols << 19 |
+// nvalid << 23 | full << 29 (full: all 32 slots valid).
 struct Chunk {
     int32_t base, stride, nrows, ncols, nvalid;
+    bool full;
 };
 
-// Walk state over the kept keys of one query tile.  Lane i of desc0/desc1
-// holds the decoded list entry cache_base + i: token base of the tile, and
-// stride | rows << 16 | cols << 24.
-struct Cursor {
-    int32_t cnext, cend;   // leading contiguous token run [cnext, cend)
-    int32_t j, cnt;        // position in the kept-tile list
-    int32_t half;          // which half (rows 0-3 / 4-7) of tile j comes next
-    const int32_t* idx;
-    int32_t cache_base;
-    int32_t desc0, desc1;
-};
-
-// Decode list entries cache_base .. cache_base+63 (one per lane).  Entries are
-// documented to be valid tile ids; out-of-range ids are clamped so that a bad
-// list cannot address outside the cache.
-__device__ __forceinline__ void cursor_fill(Cursor& c, const DevGeom& g, int lane) {
-    c.cache_base = c.j;
-    const int e = c.j + lane;
-    int id = e < c.cnt ? c.idx[e] : 0;
-    id = min(max(id, 0), g.tile_base[g.n_scales] - 1);
-    int tb = 0, side = g.side[0], off = 0, nb = g.nb[0];
-    for (int s = 1; s < g.n_scales; ++s) {
-        if (id >= g.tile_base[s]) {
-            tb = g.tile_base[s];
-            side = g.side[s];
-            off = g.tok_off[s];
-            nb = g.nb[s];
-        }
-    }
-    const int local = id - tb;
-    int a = (int)(((float)local + 0.5f) / (float)nb);
-    a -= (a * nb > local);
-    a += ((a + 1) * nb <= local);
-    const int b = local - a * nb, t = g.tile;
-    const int rows = min(t, side - a * t), cols = min(t, side - b * t);
-    c.desc0 = off + a * t * side + b * t;
-    c.desc1 = side | (rows << 16) | (cols << 24);
+__device__ __forceinline__ uint32_t pack_info(int stride, int nrows, int ncols, int nvalid) {
+    const uint32_t full = (nrows == 4 && ncols == 8 && nvalid == 32) ? 1u : 0u;
+    return (uint32_t)stride | ((uint32_t)nrows << 16) | ((uint32_t)ncols << 19) | ((uint32_t)nvalid << 23) |
+           (full << 29);
 }
 
-__device__ __forceinline__ bool cursor_next(Cursor& c, const DevGeom& g, Chunk& out, int lane) {
-    if (c.cnext < c.cend) {
-        out.base = c.cnext;
-        out.stride = 8;
-        out.nrows = 4;
-        out.ncols = 8;
-        out.nvalid = min(32, c.cend - c.cnext);
-        c.cnext += 32;
-        return true;
+__device__ __forceinline__ Chunk unpack_chunk(int32_t base, uint32_t info) {
+    Chunk c;
+    c.base = base;
+    c.stride = info & 0xffff;
+    c.nrows = (info >> 16) & 7;
+    c.ncols = (info >> 19) & 15;
+    c.nvalid = (info >> 23) & 63;
+    c.full = (info >> 29) & 1;
+    return c;
+}
+
+constexpr int kTableCap = 512;   // chunk descriptors per table build
+
+// Walk state of one query tile: what remains to be put into the table.
+struct Walk {
+    int32_t cnext, cend;   // leading contiguous token run [cnext, cend)
+    int32_t j, cnt;        // next list entry, list length
+    const int32_t* idx;
+};
+
+// Wave 0 fills the chunk table with the next descriptors of the walk (the
+// contiguous run first, then tile halves in list order) and returns how many
+// it wrote; list entries are decoded one per lane and placed with a
+// ballot prefix sum (every entry gives 1 or 2 chunks).  Entries are
+// documented to be valid tile ids; out-of-range ids are clamped so that a bad
+// list cannot address outside the cache.
+__device__ __forceinline__ int build_table(Walk& w, const DevGeom& g, uint2* table, int lane) {
+    int n = 0;
+    if (w.cnext < w.cend) {
+        const int nc = min((w.cend - w.cnext + 31) >> 5, kTableCap);
+        for (int k = lane; k < nc; k += 64) {
+            const int base = w.cnext + 32 * k;
+            table[k] = make_uint2((uint32_t)base, pack_info(8, 4, 8, min(32, w.cend - base)));
+        }
+        w.cnext = min(w.cend, w.cnext + 32 * nc);
+        n = nc;
     }
-    if (c.j >= c.cnt) return false;
-    if (c.j - c.cache_base >= 64) cursor_fill(c, g, lane);
-    const int slot = c.j - c.cache_base;
-    const int base = __builtin_amdgcn_readlane(c.desc0, slot);
-    const int info = __builtin_amdgcn_readlane(c.desc1, slot);
-    const int side = info & 0xffff, rows = (info >> 16) & 0xff, cols = info >> 24;
-    const int r0 = 4 * c.half;
-    out.base = base + r0 * side;
-    out.stride = side;
-    out.nrows = min(4, rows - r0);
-    out.ncols = cols;
-    out.nvalid = 32;
-    if (c.half == 0 && rows > 4) {
-        c.half = 1;
-    } else {
-        c.half = 0;
-        ++c.j;
+    while (w.j < w.cnt && kTableCap - n >= 128) {
+        const int e = w.j + lane;
+        const bool valid = e < w.cnt;
+        int id = valid ? w.idx[e] : 0;
+        id = min(max(id, 0), g.tile_base[g.n_scales] - 1);
+        int tb = 0, side = g.side[0], off = 0, nb = g.nb[0];
+        for (int s = 1; s < g.n_scales; ++s) {
+            if (id >= g.tile_base[s]) {
+                tb = g.tile_base[s];
+                side = g.side[s];
+                off = g.tok_off[s];
+                nb = g.nb[s];
+            }
+        }
+        const int local = id - tb;
+        int a = (int)(((float)local + 0.5f) / (float)nb);
+        a -= (a * nb > local);
+        a += ((a + 1) * nb <= local);
+        const int b = local - a * nb, t = g.tile;
+        const int rows = min(t, side - a * t), cols = min(t, side - b * t);
+        const int base = off + a * t * side + b * t;
+        const bool two = valid && rows > 4;
+        const uint64_t vb = __ballot(valid), tb2 = __ballot(two);
+        const uint64_t lt = (1ull << lane) - 1;
+        const int pos = n + __popcll(vb & lt) + __popcll(tb2 & lt);
+        if (valid) {
+            table[pos] = make_uint2((uint32_t)base, pack_info(side, min(4, rows), cols, 32));
+            if (two) table[pos + 1] = make_uint2((uint32_t)(base + 4 * side), pack_info(side, rows - 4, cols, 32));
+        }
+        n += __popcll(vb) + __popcll(tb2);
+        w.j = min(w.cnt, w.j + 64);
     }
-    return true;
+    return n;
 }
 
 // Per-lane constants of the chunk loads.  A wave fills key rows
@@ -119,48 +130,62 @@ struct LoadPlan {
     static constexpr int RPL = 1024 / ROWB;     // rows per wave-wide load
     static constexpr int LOADS = 16 / RPL;      // loads per wave per tensor
     int32_t kc[LOADS], vc[LOADS];   // col * row_bytes + unit offset (K, V)
-    int32_t lu[LOADS];              // unit offset alone (clamped slots)
-    int32_t col[LOADS];             // token column within the chunk row
-    int32_t slot[LOADS];            // key slot 0..31
 };
+
+template <int D>
+__device__ __forceinline__ int plan_slot(int wave, int lane, int i) {
+    using P = LoadPlan<D>;
+    return 16 * wave + i * P::RPL + lane / P::CH;          // key slot 0..31 filled by this lane
+}
+
+template <int D>
+__device__ __forceinline__ int plan_unit(int slot, int lane) {
+    using P = LoadPlan<D>;
+    return (lane % P::CH) ^ swz<P::CH>(slot);             // swizzled 16-byte unit
+}
 
 template <int D>
 __device__ __forceinline__ void make_plan(LoadPlan<D>& p, int wave, int lane, int64_t sk_t, int64_t sv_t) {
     using P = LoadPlan<D>;
 #pragma unroll
     for (int i = 0; i < P::LOADS; ++i) {
-        const int row = 16 * wave + i * P::RPL + lane / P::CH;
-        const int unit = (lane % P::CH) ^ swz<P::CH>(row);
-        p.slot[i] = row;
-        p.col[i] = row & 7;
-        p.lu[i] = unit * 16;
+        const int row = plan_slot<D>(wave, lane, i);
+        const int unit = plan_unit<D>(row, lane);
         p.kc[i] = (row & 7) * (int32_t)(sk_t * 2) + unit * 16;
         p.vc[i] = (row & 7) * (int32_t)(sv_t * 2) + unit * 16;
         // opaque to the optimizer: keeps the per-chunk address at one add
         // instead of a re-associated per-lane multiply
-        asm volatile("" : "+v"(p.kc[i]), "+v"(p.vc[i]), "+v"(p.lu[i]));
+        asm volatile("" : "+v"(p.kc[i]), "+v"(p.vc[i]));
     }
 }
 
 template <int D>
 __device__ __forceinline__ void load_chunk(const LoadPlan<D>& p, const __bf16* kh, const __bf16* vh, int32_t krb,
                                            int32_t vrb, const Chunk& c, uint32_t k_lds, uint32_t v_lds,
-                                           int wave) {
+                                           int wave, int lane) {
     using P = LoadPlan<D>;
-    const bool full = c.nrows == 4 && c.ncols == 8 && c.nvalid == 32;
+    if (c.full) {
 #pragma unroll
-    for (int i = 0; i < P::LOADS; ++i) {
-        const int r = (16 * wave + i * P::RPL) >> 3;     // chunk row of this load (wave-uniform)
-        const int32_t ks = (c.base + r * c.stride) * krb, vs_ = (c.base + r * c.stride) * vrb;
-        int32_t ko = ks + p.kc[i], vo = vs_ + p.vc[i];
-        if (!full) {
-            const bool valid = r < c.nrows && p.col[i] < c.ncols && p.slot[i] < c.nvalid;
-            ko = valid ? ko : c.base * krb + p.lu[i];
-            vo = valid ? vo : c.base * vrb + p.lu[i];
+        for (int i = 0; i < P::LOADS; ++i) {
+            const int r = (16 * wave + i * P::RPL) >> 3;     // chunk row of this load (wave-uniform)
+            const int32_t t0 = c.base + r * c.stride;
+            const uint32_t dst = (uint32_t)((16 * wave + i * P::RPL) * P::ROWB);
+            lds_dma16_off(kh, t0 * krb + p.kc[i], __builtin_amdgcn_readfirstlane(k_lds + dst));
+            lds_dma16_off(vh, t0 * vrb + p.vc[i], __builtin_amdgcn_readfirstlane(v_lds + dst));
         }
-        const uint32_t dst = (uint32_t)((16 * wave + i * P::RPL) * P::ROWB);
-        lds_dma16_off(kh, ko, __builtin_amdgcn_readfirstlane(k_lds + dst));
-        lds_dma16_off(vh, vo, __builtin_amdgcn_readfirstlane(v_lds + dst));
+    } else {
+#pragma unroll
+        for (int i = 0; i < P::LOADS; ++i) {
+            const int slot = plan_slot<D>(wave, lane, i);
+            const int r = slot >> 3, col = slot & 7;
+            const int unit16 = plan_unit<D>(slot, lane) * 16;
+            // padding slots re-read the chunk's first token (finite values; masked later)
+            const bool valid = r < c.nrows && col < c.ncols && slot < c.nvalid;
+            const int32_t tok = valid ? c.base + r * c.stride + col : c.base;
+            const uint32_t dst = (uint32_t)((16 * wave + i * P::RPL) * P::ROWB);
+            lds_dma16_off(kh, tok * krb + unit16, __builtin_amdgcn_readfirstlane(k_lds + dst));
+            lds_dma16_off(vh, tok * vrb + unit16, __builtin_amdgcn_readfirstlane(v_lds + dst));
+        }
     }
 }
 
@@ -182,7 +207,11 @@ __device__ __forceinline__ float half_swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Consume one chunk of 32 keys from LDS (kst: K rows, vst: V rows).
+// Consume one chunk of 32 keys from LDS (kst: K rows, vst: V rows).  The
+// LDS operand reads of each phase are issued ahead of the MFMAs that consume
+// them (all K rows before S^T, all V^T reads before the softmax, so they land
+// while it runs); scheduling barriers keep the compiler from moving them back
+// next to their uses.
 template <int D>
 __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __restrict__ kst,
                                              const char* __restrict__ vst, const Chunk& cc, float c, int lane) {
@@ -194,15 +223,43 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
     const int n = lane & 31, g = lane >> 5;
 
     // S^T (32 keys x 32 queries) = K Q^T
-    f32x16 sacc = (f32x16)0.0f;
+    bf16x8 kop[KSTEPS];
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
         const int pc = (2 * s + g) ^ swz<CH>(n);
-        const bf16x8 kop = *(const bf16x8*)(kst + n * ROWB + pc * 16);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, st.qreg[s], sacc, 0, 0, 0);
+        kop[s] = *(const bf16x8*)(kst + n * ROWB + pc * 16);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sacc = (f32x16)0.0f;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s], st.qreg[s], sacc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // V^T operands for the whole chunk (transposing LDS reads), in flight during the softmax
+    const int c16 = lane >> 4, p16 = lane & 15;
+    const int half = c16 & 1, r4 = p16 >> 2, q4 = p16 & 3;
+    bf16x8 vop[MBLK][2];
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb) {
+        const int d = 32 * mb + 16 * half + 4 * q4;
+        const int lc = d >> 3, within = (d & 7) * 2;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            bf16x4 part[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int row = 16 * t + 8 * jj + 4 * g + r4;
+                const char* addr = vst + row * ROWB + ((lc ^ swz<CH>(row)) << 4) + within;
+                part[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4*)(addr));
+            }
+            vop[mb][t] = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     // padding keys of partial chunks -> -inf (value i sits at row i/4, column 4g + i%4)
-    if (cc.nrows < 4 || cc.ncols < 8 || cc.nvalid < 32) {
+    if (!cc.full) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int r = i >> 2, col = 4 * g + (i & 3), key = 8 * r + col;
@@ -231,27 +288,14 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
         st.l_run += p;
         pt[i >> 3][i & 7] = (__bf16)p;
     }
-    // O^T (D x 32 queries) += V^T P^T, V^T through transposing LDS reads
-    const int c16 = lane >> 4, p16 = lane & 15;
-    const int half = c16 & 1, r4 = p16 >> 2, q4 = p16 & 3;
+    __builtin_amdgcn_sched_barrier(0);
+
+    // O^T (D x 32 queries) += V^T P^T
 #pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb) {
-        const int d = 32 * mb + 16 * half + 4 * q4;
-        const int lc = d >> 3, within = (d & 7) * 2;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            bf16x4 part[2];
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int row = 16 * t + 8 * jj + 4 * g + r4;
-                const char* addr = vst + row * ROWB + ((lc ^ swz<CH>(row)) << 4) + within;
-                part[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (__attribute__((address_space(3))) bf16x4*)(addr));
-            }
-            const bf16x8 vop = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-            st.oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pt[t], st.oacc[mb], 0, 0, 0);
-        }
-    }
+        for (int mb = 0; mb < MBLK; ++mb)
+            st.oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[mb][t], pt[t], st.oacc[mb], 0, 0, 0);
 }
 
 template <int D, bool DENSE>
@@ -259,8 +303,8 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     constexpr int KSTEPS = D / 16;
     constexpr int MBLK = D / 32;
     constexpr int STAGE = 32 * D * 2;
-    constexpr int LOADS = 2 * LoadPlan<D>::LOADS;   // vm instructions per wave per chunk
     __shared__ __attribute__((aligned(1024))) char smem[4 * STAGE];   // [stage][K, V]
+    __shared__ uint2 table[DENSE ? 1 : kTableCap];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n = lane & 31, g = lane >> 5;  // query column and lane half of this lane
@@ -282,39 +326,33 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         const int ti = qt / nbq, tj = qt - ti * nbq;
         tok = (int64_t)(8 * ti + 4 * wave + (n >> 3)) * a.q_side + 8 * tj + (n & 7);
     }
-    WaveState<D> st;
-    const __bf16* qp = a.q + b * a.sq_b + h * a.sq_h + tok * a.sq_t;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) st.qreg[s] = *(const bf16x8*)(qp + 16 * s + 8 * g);
-#pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] = (f32x16)0.0f;
-    st.m_run = -INFINITY;
-    st.l_run = 0.0f;
     const __bf16* kh = a.k + b * a.sk_b + h * a.sk_h;
     const __bf16* vh = a.v + b * a.sv_b + h * a.sv_h;
     const int32_t krb = (int32_t)(a.sk_t * 2), vrb = (int32_t)(a.sv_t * 2);
-    LoadPlan<D> plan;
-    make_plan<D>(plan, wave, lane, a.sk_t, a.sv_t);
+    const float c = a.scale_log2;
+    const uint32_t lds0 = lds_addr(smem);
+    const char* sm = smem;
 
-    // ---- kept-key walk
-    Cursor cur;
-    cur.half = 0;
+    // ---- the walk, in table builds of up to kTableCap chunks (the first one
+    // before the accumulators are live)
+    Walk w;
+    __shared__ int table_n;
+    int nch;
     if (DENSE) {
-        cur.cnext = 0;
-        cur.cend = (int32_t)a.nk;
-        cur.j = cur.cnt = 0;
-        cur.idx = nullptr;
-        cur.cache_base = 0;
-        cur.desc0 = cur.desc1 = 0;
+        w.cnext = 0;
+        w.cend = (int32_t)a.nk;
+        w.j = w.cnt = 0;
+        w.idx = nullptr;
+        nch = (w.cend + 31) >> 5;
     } else {
         const int64_t row = (a.per_head ? (int64_t)bh * a.nqb : 0) + qt;
-        cur.cnt = a.kv_cnt[row];
-        cur.idx = a.kv_idx + row * a.nkb;
+        w.cnt = a.kv_cnt[row];
+        w.idx = a.kv_idx + row * a.nkb;
         // leading run of tiles 0,1,2,...: whole scales kept from the start form
         // one contiguous token range
         int p = 0;
         for (;;) {
-            const int v = (p + lane < cur.cnt) ? cur.idx[p + lane] : -1;
+            const int v = (p + lane < w.cnt) ? w.idx[p + lane] : -1;
             const uint64_t off = __ballot(v != p + lane);
             if (off) {
                 p += __builtin_ctzll(off);
@@ -324,46 +362,85 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         }
         int s = 0;
         while (s < a.g.n_scales && a.g.tile_base[s + 1] <= p) ++s;
-        cur.cnext = 0;
-        cur.cend = a.g.tok_off[s];
-        cur.j = a.g.tile_base[s];
-        cursor_fill(cur, a.g, lane);
+        w.cnext = 0;
+        w.cend = a.g.tok_off[s];
+        w.j = a.g.tile_base[s];
+        if (wave == 0) {
+            const int nb = build_table(w, a.g, table, lane);
+            if (lane == 0) table_n = nb;
+        }
+        __syncthreads();   // table visible to both waves
+        nch = __builtin_amdgcn_readfirstlane(table_n);
     }
-    wait_vmcnt(0);   // Q and the first list entries are in registers before LDS-DMA traffic starts
-    const float c = a.scale_log2;
 
-    const uint32_t lds0 = lds_addr(smem);
-    const char* sm = smem;
-    Chunk cc, cn;
-    bool have = cursor_next(cur, a.g, cc, lane);
-    if (have) load_chunk<D>(plan, kh, vh, krb, vrb, cc, lds0, lds0 + STAGE, wave);
-    while (have) {
-        // stage 0 holds chunk cc; prefetch the next one into stage 1
-        bool more = cursor_next(cur, a.g, cn, lane);
-        if (more) {
-            load_chunk<D>(plan, kh, vh, krb, vrb, cn, lds0 + 2 * STAGE, lds0 + 3 * STAGE, wave);
-            wait_vmcnt(LOADS);
-        } else {
-            wait_vmcnt(0);
+    WaveState<D> st;
+    const __bf16* qp = a.q + b * a.sq_b + h * a.sq_h + tok * a.sq_t;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) st.qreg[s] = *(const bf16x8*)(qp + 16 * s + 8 * g);
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] = (f32x16)0.0f;
+    st.m_run = -INFINITY;
+    st.l_run = 0.0f;
+    LoadPlan<D> plan;
+    make_plan<D>(plan, wave, lane, a.sk_t, a.sv_t);
+
+    while (nch > 0) {
+        // descriptors of chunks [win, win + 64) in registers, lane i = chunk win + i
+        int win = 0;
+        uint32_t d0 = 0, d1 = 0;
+        if (!DENSE) {
+            const uint2 t = table[min(lane, kTableCap - 1)];
+            d0 = t.x;
+            d1 = t.y;
         }
-        wg_barrier();
-        attend_chunk<D>(st, sm, sm + STAGE, cc, c, lane);
-        wg_barrier();
-        if (!more) break;
-        cc = cn;
-        // stage 1 holds chunk cc; prefetch the next one into stage 0
-        more = cursor_next(cur, a.g, cn, lane);
-        if (more) {
-            load_chunk<D>(plan, kh, vh, krb, vrb, cn, lds0, lds0 + STAGE, wave);
-            wait_vmcnt(LOADS);
-        } else {
+        auto desc = [&](int ci) -> Chunk {
+            if (DENSE) {
+                const int base = 32 * ci;
+                return unpack_chunk(base, pack_info(8, 4, 8, min(32, w.cend - base)));
+            }
+            if (ci - win >= 64) {
+                win += 64;
+                const uint2 t = table[min(win + lane, kTableCap - 1)];
+                d0 = t.x;
+                d1 = t.y;
+            }
+            return unpack_chunk((int32_t)__builtin_amdgcn_readlane(d0, ci - win),
+                                __builtin_amdgcn_readlane(d1, ci - win));
+        };
+
+        // two LDS stages, one barrier per chunk: after it, every wave has its
+        // loads of this chunk in LDS and has finished the previous chunk, whose
+        // stage then takes the next prefetch
+        Chunk cur = desc(0), nxt;
+        load_chunk<D>(plan, kh, vh, krb, vrb, cur, lds0, lds0 + STAGE, wave, lane);
+        for (int ci = 0; ci < nch; ci += 2) {
             wait_vmcnt(0);
+            wg_barrier();
+            if (ci + 1 < nch) {
+                nxt = desc(ci + 1);
+                load_chunk<D>(plan, kh, vh, krb, vrb, nxt, lds0 + 2 * STAGE, lds0 + 3 * STAGE, wave, lane);
+            }
+            attend_chunk<D>(st, sm, sm + STAGE, cur, c, lane);
+            if (ci + 1 >= nch) break;
+            cur = nxt;
+            wait_vmcnt(0);
+            wg_barrier();
+            if (ci + 2 < nch) {
+                nxt = desc(ci + 2);
+                load_chunk<D>(plan, kh, vh, krb, vrb, nxt, lds0, lds0 + STAGE, wave, lane);
+            }
+            attend_chunk<D>(st, sm + 2 * STAGE, sm + 3 * STAGE, cur, c, lane);
+            cur = nxt;
         }
-        wg_barrier();
-        attend_chunk<D>(st, sm + 2 * STAGE, sm + 3 * STAGE, cc, c, lane);
-        wg_barrier();
-        cc = cn;
-        have = more;
+        if (DENSE) break;
+        // long lists: rebuild the table with what remains of the walk
+        __syncthreads();   // every wave done with the table and the stages
+        if (wave == 0) {
+            const int nb = build_table(w, a.g, table, lane);
+            if (lane == 0) table_n = nb;
+        }
+        __syncthreads();
+        nch = __builtin_amdgcn_readfirstlane(table_n);
     }
 
     // ---- epilogue
