@@ -115,8 +115,7 @@ int varsparse_map_indices(const varsparse_geom* geom, int32_t d_scale, int32_t t
     const int nqbT = gT.nb[t_scale] * gT.nb[t_scale], nkbT = gT.tile_base[t_scale + 1];
     if (nkbD > 256) return VARSPARSE_EUNSUPPORTED;
     const int words = (nkbD + 31) / 32;
-    if ((int64_t)nqbD * words * 4 > 32768) return VARSPARSE_EUNSUPPORTED;
-    if ((int64_t)B * H > 0x7fffffff / std::max(nqbD, 1)) return VARSPARSE_EINVAL;
+    if ((int64_t)B * H * std::max(nqbD, (nqbT + 3) / 4) > 0x7fffffff) return VARSPARSE_EINVAL;
     if (q_d != nullptr) {
         if (dtype != VARSPARSE_BF16) return VARSPARSE_EUNSUPPORTED;
         if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;

@@ -11,9 +11,9 @@
 // partials.  The QK^T work is the bf16 MFMA tile engine of the attention
 // kernel.  Reductions run in a fixed order: scores are bit-reproducible.
 //
-// cs4a_select_map_kernel: one workgroup per (batch, head).  Top-p on
-// integer-quantised scores (exact, associative), kept as a bitset in LDS,
-// then the target-scale lists: parent tile by floor scaling, tiles below the
+// cs4a_select_map_kernel: one wave per (batch, head, target query tile).
+// Top-p on integer-quantised scores (exact, associative) of the parent
+// decision tile, kept as a bitset in registers, then the target-scale lists: parent tile by floor scaling, tiles below the
 // decision scale copied, decision-scale tiles expanded to their footprint on
 // every scale from D to the target, sink tiles added.
 #include "kernel_args.h"
@@ -154,94 +154,113 @@ __device__ __forceinline__ int64_t quantise(float s) {
     return x >= 0.0f ? (int64_t)floorf(x) : 0;
 }
 
+// One workgroup = 4 waves = 4 target query tiles of one (batch, head).  Each
+// wave selects the key tiles of its parent decision tile (scores staged in
+// LDS, one quantised score per entry; ranks and prefix masses by broadcast
+// reads), keeps the selection as a bitset in registers (one ballot per 64
+// tiles), then decides every target key tile and compacts the list with
+// ballots.  The wave whose target tile is the first child of its parent also
+// writes the parent's selection (sel_cnt / sel_idx) when asked to.
 __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a) {
-    extern __shared__ uint32_t selbits[];   // [nqbD][words]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int bh = blockIdx.x;
+    __shared__ int64_t mq[4][256];   // quantised scores of each wave's parent tile
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int groups = (a.nqbT + 3) / 4;
+    const int bh = blockIdx.x / groups;
+    const int qt = (blockIdx.x - bh * groups) * 4 + wave;
+    if (qt >= a.nqbT) return;   // whole wave leaves; no workgroup barrier below
     const int nkbD = a.nkbD;
+    const int D = a.d_scale, t = a.g.tile;
+    const int hD = a.g.side[D], nbD = a.g.nb[D], nbT = a.g.nb[a.t_scale];
+    const int ti = qt / nbT, tj = qt - ti * nbT;
+    const int pi = ti * nbD / nbT, pj = tj * nbD / nbT;
+    const int parent = pi * nbD + pj;
 
-    // ---- top-p selection, one wave per decision query tile
-    for (int qd = wave; qd < a.nqbD; qd += 4) {
-        const float* sc = a.scores + ((int64_t)bh * a.nqbD + qd) * nkbD;
-        int64_t tot = 0;
-        for (int j = lane; j < nkbD; j += 64) tot += quantise(sc[j]);
-        for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
-        const double thr = ceil(a.top_p * (double)tot);
-        int base = 0;
-        for (int c0 = 0; c0 < nkbD; c0 += 64) {
-            const int j = c0 + lane;
-            bool keep = false;
+    // ---- top-p selection of the parent tile
+    const float* sc = a.scores + ((int64_t)bh * a.nqbD + parent) * nkbD;
+    int64_t tot = 0;
+    for (int j = lane; j < nkbD; j += 64) {
+        const int64_t m = quantise(sc[j]);
+        mq[wave][j] = m;
+        tot += m;
+    }
+    for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+    const double thr = ceil(a.top_p * (double)tot);
+    uint64_t sel[4] = {0, 0, 0, 0};   // bit j of the selection, 64 tiles per word
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+        const int j = 64 * w4 + lane;
+        bool keep = false;
+        if (64 * w4 < nkbD) {
             if (j < nkbD) {
-                const int64_t mj = quantise(sc[j]);
+                const int64_t mj = mq[wave][j];
                 int64_t before = 0;
                 for (int i = 0; i < nkbD; ++i) {
-                    const int64_t mi = quantise(sc[i]);
-                    if (mi > mj || (mi == mj && i < j)) before += mi;
+                    const int64_t mi = mq[wave][i];
+                    before += (mi > mj || (mi == mj && i < j)) ? mi : 0;
                 }
                 keep = (double)before < thr;
             }
-            const uint64_t bal = __ballot(keep);
-            if (lane == 0) {
-                selbits[qd * a.words + c0 / 32] = (uint32_t)bal;
-                if (c0 / 32 + 1 < a.words) selbits[qd * a.words + c0 / 32 + 1] = (uint32_t)(bal >> 32);
-            }
-            if (a.sel_idx != nullptr && keep)
-                a.sel_idx[((int64_t)bh * a.nqbD + qd) * nkbD + base + __popcll(bal & ((1ull << lane) - 1))] = j;
-            base += __popcll(bal);
-        }
-        if (a.sel_idx != nullptr) {
-            for (int j = base + lane; j < nkbD; j += 64) a.sel_idx[((int64_t)bh * a.nqbD + qd) * nkbD + j] = -1;
-            if (lane == 0) a.sel_cnt[(int64_t)bh * a.nqbD + qd] = base;
+            sel[w4] = __ballot(keep);
         }
     }
-    __syncthreads();
-
-    // ---- mapping onto the target scale, one wave per target query tile
-    const int D = a.d_scale, t = a.g.tile;
-    const int hD = a.g.side[D], nbD = a.g.nb[D], nbT = a.g.nb[a.t_scale];
-    for (int qt = wave; qt < a.nqbT; qt += 4) {
-        const int ti = qt / nbT, tj = qt - ti * nbT;
-        const int parent = (ti * nbD / nbT) * nbD + (tj * nbD / nbT);
-        const uint32_t* bits = selbits + parent * a.words;
+    const bool first_row = ti == 0 || (ti - 1) * nbD / nbT != pi;
+    const bool first_col = tj == 0 || (tj - 1) * nbD / nbT != pj;
+    if (a.sel_idx != nullptr && first_row && first_col) {
         int base = 0;
-        for (int c0 = 0; c0 < a.nkbT; c0 += 64) {
-            const int j = c0 + lane;
-            bool keep = false;
-            if (j < a.nkbT) {
-                const int s = scale_of_tile(a.g, j);
-                if (s < a.n_sink) {
-                    keep = true;
-                } else if (s < D) {
-                    keep = (bits[j >> 5] >> (j & 31)) & 1u;
-                } else {
-                    const int hs = a.g.side[s], nbs = a.g.nb[s];
-                    const int local = j - a.g.tile_base[s];
-                    const int ka = local / nbs, kb = local - ka * nbs;
-                    const int klo_y = ka * t, khi_y = min(ka * t + t, hs) - 1;
-                    const int klo_x = kb * t, khi_x = min(kb * t + t, hs) - 1;
-                    for (int sa = 0; sa < nbD && !keep; ++sa) {
-                        const int ey = min(sa * t + t, hD);
-                        const int lo_y = (int)(((int64_t)sa * t * hs) / hD);
-                        const int hi_y = (int)(((int64_t)ey * hs + hD - 1) / hD) - 1;
-                        if (klo_y > hi_y || lo_y > khi_y) continue;
-                        for (int sb = 0; sb < nbD; ++sb) {
-                            const int sid = a.g.tile_base[D] + sa * nbD + sb;
-                            if (!((bits[sid >> 5] >> (sid & 31)) & 1u)) continue;
-                            const int ex = min(sb * t + t, hD);
-                            const int lo_x = (int)(((int64_t)sb * t * hs) / hD);
-                            const int hi_x = (int)(((int64_t)ex * hs + hD - 1) / hD) - 1;
-                            if (klo_x <= hi_x && lo_x <= khi_x) { keep = true; break; }
-                        }
+        int32_t* out = a.sel_idx + ((int64_t)bh * a.nqbD + parent) * nkbD;
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+            const int j = 64 * w4 + lane;
+            if ((sel[w4] >> lane) & 1) out[base + __popcll(sel[w4] & ((1ull << lane) - 1))] = j;
+            base += __popcll(sel[w4]);
+        }
+        for (int j = base + lane; j < nkbD; j += 64) out[j] = -1;
+        if (lane == 0) a.sel_cnt[(int64_t)bh * a.nqbD + parent] = base;
+    }
+    auto selected = [&](int id) -> bool {
+        const uint64_t word = id < 64 ? sel[0] : id < 128 ? sel[1] : id < 192 ? sel[2] : sel[3];
+        return (word >> (id & 63)) & 1;
+    };
+
+    // ---- mapping onto the target scale
+    int base = 0;
+    int32_t* out = a.kv_idx + ((int64_t)bh * a.nqbT + qt) * a.nkbT;
+    for (int c0 = 0; c0 < a.nkbT; c0 += 64) {
+        const int j = c0 + lane;
+        bool keep = false;
+        if (j < a.nkbT) {
+            const int s = scale_of_tile(a.g, j);
+            if (s < a.n_sink) {
+                keep = true;
+            } else if (s < D) {
+                keep = selected(j);
+            } else {
+                const int hs = a.g.side[s], nbs = a.g.nb[s];
+                const int local = j - a.g.tile_base[s];
+                const int ka = local / nbs, kb = local - ka * nbs;
+                const int klo_y = ka * t, khi_y = min(ka * t + t, hs) - 1;
+                const int klo_x = kb * t, khi_x = min(kb * t + t, hs) - 1;
+                for (int sa = 0; sa < nbD && !keep; ++sa) {
+                    const int ey = min(sa * t + t, hD);
+                    const int lo_y = (int)(((int64_t)sa * t * hs) / hD);
+                    const int hi_y = (int)(((int64_t)ey * hs + hD - 1) / hD) - 1;
+                    if (klo_y > hi_y || lo_y > khi_y) continue;
+                    for (int sb = 0; sb < nbD; ++sb) {
+                        if (!selected(a.g.tile_base[D] + sa * nbD + sb)) continue;
+                        const int ex = min(sb * t + t, hD);
+                        const int lo_x = (int)(((int64_t)sb * t * hs) / hD);
+                        const int hi_x = (int)(((int64_t)ex * hs + hD - 1) / hD) - 1;
+                        if (klo_x <= hi_x && lo_x <= khi_x) { keep = true; break; }
                     }
                 }
             }
-            const uint64_t bal = __ballot(keep);
-            if (keep) a.kv_idx[((int64_t)bh * a.nqbT + qt) * a.nkbT + base + __popcll(bal & ((1ull << lane) - 1))] = j;
-            base += __popcll(bal);
         }
-        for (int j = base + lane; j < a.nkbT; j += 64) a.kv_idx[((int64_t)bh * a.nqbT + qt) * a.nkbT + j] = -1;
-        if (lane == 0) a.kv_cnt[(int64_t)bh * a.nqbT + qt] = base;
+        const uint64_t bal = __ballot(keep);
+        if (keep) out[base + __popcll(bal & ((1ull << lane) - 1))] = j;
+        base += __popcll(bal);
     }
+    for (int j = base + lane; j < a.nkbT; j += 64) out[j] = -1;
+    if (lane == 0) a.kv_cnt[(int64_t)bh * a.nqbT + qt] = base;
 }
 
 hipError_t launch_cs4a_score(const ScoreArgs& a, int head_dim, hipStream_t stream) {
@@ -263,8 +282,8 @@ hipError_t launch_cs4a_score(const ScoreArgs& a, int head_dim, hipStream_t strea
 }
 
 hipError_t launch_cs4a_select_map(const SelMapArgs& a, int bh, hipStream_t stream) {
-    const size_t shmem = (size_t)a.nqbD * a.words * sizeof(uint32_t);
-    hipLaunchKernelGGL(cs4a_select_map_kernel, dim3(bh), dim3(256), shmem, stream, a);
+    const int groups = (a.nqbT + 3) / 4;
+    hipLaunchKernelGGL(cs4a_select_map_kernel, dim3(bh * groups), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
