@@ -29,6 +29,24 @@ import numpy as np
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per launch of the sparse attention kernel on this workload, from
+# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by a 256 MiB copy
+# (x2.000 and x1.000), recorded with the SHA-256 of the kernel sources they
+# were taken on; reported only while those sources are unchanged.
+TRAFFIC = {"bytes": 368.7e6, "sources_sha256": "da94f4ae2fb65d2aa4c876d6085eff88338a7bd2b584c1cab196ddb7c3b5ea71"}
+KERNEL_SOURCES = ("block_sparse_cross_csla_amd/csrc/attn_bf16.hip", "block_sparse_cross_csla_amd/csrc/common.h",
+                  "block_sparse_cross_csla_amd/csrc/kernel_args.h")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -172,7 +190,8 @@ def main():
         "block_sparsity": {"count": float(count_sparsity), "flop": float(flop_sparsity)},
         "roofline": {"bound": "mfma", "achieved": flops / (attn_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                     "traffic": None, "kernel": "attn_fwd_bf16_kernel<128,false>",
+                     "traffic": TRAFFIC["bytes"] if kernel_sources_sha256() == TRAFFIC["sources_sha256"] else None,
+                     "traffic_unit": "bytes per launch", "kernel": "attn_fwd_bf16_kernel<128,false>",
                      "flop_per_launch": flops},
     }
 
