@@ -113,7 +113,7 @@ int varsparse_map_indices(const varsparse_geom* geom, int32_t d_scale, int32_t t
     const vs::DevGeom gT = vs::make_dev_geom(*geom, t_scale);
     const int nqbD = gD.nb[d_scale] * gD.nb[d_scale], nkbD = gD.tile_base[d_scale + 1];
     const int nqbT = gT.nb[t_scale] * gT.nb[t_scale], nkbT = gT.tile_base[t_scale + 1];
-    if (nkbD > 256) return VARSPARSE_EUNSUPPORTED;
+    if (nkbD > 240) return VARSPARSE_EUNSUPPORTED;
     const int words = (nkbD + 31) / 32;
     if ((int64_t)B * H * std::max(nqbD, (nqbT + 3) / 4) > 0x7fffffff) return VARSPARSE_EINVAL;
     if (q_d != nullptr) {

@@ -99,7 +99,7 @@ int varsparse_geom_counts(const varsparse_geom* geom, int32_t q_scale,
  * Budget mode (budget > 0, radius ignored and may be NULL): per query tile
  * keep the first max(budget, sink tiles + 1) key tiles (at most nkb) ranked by
  * (not sink, admission radius, -scale, id), the admission radius being the
- * smallest window radius that keeps the pair.  Supports nkb <= 8192.
+ * smallest window radius that keeps the pair.  Supports nkb <= 4096.
  *
  * Outputs (dev): mask u8 [nqb * nkb] (1 = kept; may be NULL), kv_cnt int32
  * [nqb], kv_idx int32 [nqb * nkb] (ascending, -1 padded).  0 <= n_sink <= q_scale.
@@ -123,7 +123,7 @@ int varsparse_build_mask(const varsparse_geom* geom, int32_t q_scale, int32_t n_
  * strides k_strides.  bf16 only, head_dim in {64, 128}, tile == 8.
  * With q_d == NULL, scores are an input (a previous call's output) and k,
  * q_strides, k_strides, softmax_scale are ignored.
- * scores: dev float32 [B * H * nqb_D * nkb_D], nkb_D <= 256.
+ * scores: dev float32 [B * H * nqb_D * nkb_D], nkb_D <= 240.
  *
  * Selection: per (b, h, decision query tile) the scores are quantised to
  * m = floor(score * 2^24), ordered by (m descending, id ascending), and the
