@@ -257,6 +257,43 @@ def bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev):
         e1.record(stream)
         torch.cuda.synchronize()
         res[name] = e0.elapsed_time(e1) / n
+    # O_cache: the decision scale's residual (full minus block-sparse output
+    # over its own selection) upsampled onto each target output.  The full
+    # attention at the decision scale is the model's own and is timed apart.
+    nqb_d, nkb_d, _, nk_d = vs.geom_counts(w.sides, w.tile, D)
+    lists_d = (torch.empty(w.B, w.H, nqb_d, dtype=torch.int32, device=dev),
+               torch.empty(w.B, w.H, nqb_d, nkb_d, dtype=torch.int32, device=dev))
+    o_full_d, o_sparse_d = torch.empty_like(q_d), torch.empty_like(q_d)
+
+    def full_d():
+        vs.dense_attn_fwd(q_d, k[:, :, :nk_d], v[:, :, :nk_d], softmax_scale=scale, out=o_full_d,
+                          want_lse=False, stream=stream)
+
+    def ocache_step():
+        vs.map_indices(w.sides, w.tile, D, D, w.n_sink, W.CS4A_TOP_P, scores=scores, out=lists_d, stream=stream)
+        vs.attn_fwd(q_d, k[:, :, :nk_d], v[:, :, :nk_d], w.sides, w.tile, D, *lists_d, softmax_scale=scale,
+                    out=o_sparse_d, want_lse=False, stream=stream)
+        for T in W.CS4A_TARGETS:
+            vs.ocache_correct(o_full_d, o_sparse_d, outs[T], w.sides[D], w.sides[T], stream=stream)
+
+    T_last = W.CS4A_TARGETS[-1]
+
+    def correct_last():
+        vs.ocache_correct(o_full_d, o_sparse_d, outs[T_last], w.sides[D], w.sides[T_last], stream=stream)
+
+    step()
+    for name, fn in (("full_d", full_d), ("ocache", ocache_step), ("correct_last", correct_last)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / n
+    corr_bytes = 2 * 2 * w.B * w.H * w.d * (w.sides[T_last] ** 2 + w.sides[D] ** 2)
     flops = 0.0
     for T in W.CS4A_TARGETS:
         sizes = tile_sizes(w.sides, T, w.tile)
@@ -268,7 +305,14 @@ def bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev):
             "speedup_vs_dense": res["dense"] / res["sparse"],
             "attention_tflop_per_step": flops / 1e12,
             "effective_tflops": flops / (res["sparse"] * 1e-3) / 1e12,
-            "timed": "score + select + map (3 targets) + 3 block-sparse attentions; dense: 3 dense attentions"}
+            "timed": "score + select + map (3 targets) + 3 block-sparse attentions; dense: 3 dense attentions",
+            "ocache": {"ms_per_step": res["ocache"],
+                       "timed": "map D->D + block-sparse attention at D + 3 corrections",
+                       "decision_full_attention_ms": res["full_d"],
+                       "correct_side64_ms": res["correct_last"],
+                       "correct_side64_bytes": corr_bytes,
+                       "correct_side64_gbps": corr_bytes / (res["correct_last"] * 1e-3) / 1e9,
+                       "hbm_peak_gbps": 8000.0}}
 
 
 def cpu_baseline(w, q_np, k_np, v_np, cnt_h, idx_h, sizes, round_bf16, seconds):

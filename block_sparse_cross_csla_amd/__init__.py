@@ -21,4 +21,5 @@ from ._lib import (  # noqa: F401
     lib,
     make_geom,
     map_indices,
+    ocache_correct,
 )

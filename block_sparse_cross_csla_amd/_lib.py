@@ -23,6 +23,7 @@ EXPORTS = (
     "varsparse_map_indices",
     "varsparse_attn_fwd",
     "varsparse_dense_attn_fwd",
+    "varsparse_ocache_correct",
     "varsparse_strerror",
     "varsparse_last_hip_error",
 )
@@ -43,7 +44,7 @@ class VarsparseError(RuntimeError):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_sparse_cross_csla_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python block_sparse_cross_csla_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     PI32, PI64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
@@ -54,10 +55,11 @@ def _load():
                                           P, PI64, P, PI64, F32, P, P, P, P, P, P]
     lib.varsparse_attn_fwd.argtypes = [PG, I32, I32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32, P]
     lib.varsparse_dense_attn_fwd.argtypes = [I32, I32, I32, I32, I64, I64, P, P, P, P, P, PI64, F32, P]
+    lib.varsparse_ocache_correct.argtypes = [I32, I32, I32, I32, I32, P, P, P, PI64, P]
     lib.varsparse_strerror.argtypes = [ctypes.c_int]
     lib.varsparse_strerror.restype = ctypes.c_char_p
     lib.varsparse_last_hip_error.argtypes = []
-    for name in EXPORTS[:5]:
+    for name in EXPORTS[:6]:
         getattr(lib, name).restype = ctypes.c_int
     lib.varsparse_last_hip_error.restype = ctypes.c_int
     return lib
@@ -213,3 +215,19 @@ def dense_attn_fwd(q, k, v, softmax_scale=None, out=None, lse=None, want_lse=Tru
                                          _ptr(lse), _strides(q, k, v, out), float(scale), _stream(stream)),
            "varsparse_dense_attn_fwd")
     return out, lse
+
+
+def ocache_correct(o_full_d, o_sparse_d, o_t, side_d: int, side_t: int, stream=None):
+    """O_cache: o_t += nearest-upsampled (o_full_d - o_sparse_d), in place.
+    o_full_d / o_sparse_d [B,H,side_d^2,d], o_t [B,H,side_t^2,d], bf16."""
+    B, H, nt, d = o_t.shape
+    if o_full_d.shape != o_sparse_d.shape or o_full_d.shape[:2] != (B, H) or o_full_d.shape[3] != d:
+        raise ValueError("shape mismatch between the decision outputs and the target output")
+    if o_full_d.shape[2] != side_d * side_d or nt != side_t * side_t:
+        raise ValueError("token counts do not match the sides")
+    if any(t.stride(-1) != 1 for t in (o_full_d, o_sparse_d, o_t)):
+        raise ValueError("the head dimension must be contiguous")
+    st = (ctypes.c_int64 * 9)(*o_full_d.stride()[:3], *o_sparse_d.stride()[:3], *o_t.stride()[:3])
+    _check(_LIB.varsparse_ocache_correct(B, H, d, side_d, side_t, _ptr(o_full_d), _ptr(o_sparse_d), _ptr(o_t), st,
+                                         _stream(stream)), "varsparse_ocache_correct")
+    return o_t

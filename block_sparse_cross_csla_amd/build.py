@@ -1,6 +1,8 @@
 """Build libvarsparse.so in-tree with hipcc for gfx950.
 
-    python -m block_sparse_cross_csla_amd.build
+    python block_sparse_cross_csla_amd/build.py
+
+(run by path: importing the package loads the library this builds)
 """
 from __future__ import annotations
 
@@ -12,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvarsparse.so")
-SOURCES = ["api.hip", "attn_bf16.hip", "attn_fp32.hip", "csla_mask.hip", "cs4a.hip"]
+SOURCES = ["api.hip", "attn_bf16.hip", "attn_fp32.hip", "csla_mask.hip", "cs4a.hip", "ocache.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -241,6 +241,24 @@ int varsparse_dense_attn_fwd(varsparse_dtype dtype, int32_t B, int32_t H, int32_
     return hip_status(vs::launch_attn_fp32(a, head_dim, true, (hipStream_t)stream));
 }
 
+int varsparse_ocache_correct(int32_t B, int32_t H, int32_t head_dim, int32_t side_d, int32_t side_t,
+                             const void* o_full_d, const void* o_sparse_d, void* o_t,
+                             const int64_t strides[9], void* stream) {
+    if (B < 1 || H < 1 || side_d < 1 || side_t < side_d || side_t > 65535) return VARSPARSE_EINVAL;
+    if (head_dim < 8 || head_dim % 8 != 0 || head_dim > 1024) return VARSPARSE_EINVAL;
+    if (!o_full_d || !o_sparse_d || !o_t || !strides) return VARSPARSE_EINVAL;
+    if (!aligned16(o_full_d) || !aligned16(o_sparse_d) || !aligned16(o_t)) return VARSPARSE_EINVAL;
+    if (!strides_ok(strides, 9, 8)) return VARSPARSE_EINVAL;
+    if ((int64_t)B * H > 65535) return VARSPARSE_EUNSUPPORTED;
+    vs::OcacheArgs a{};
+    a.o_full = (const __bf16*)o_full_d; a.o_sparse = (const __bf16*)o_sparse_d; a.o_t = (__bf16*)o_t;
+    a.sf_b = strides[0]; a.sf_h = strides[1]; a.sf_t = strides[2];
+    a.sp_b = strides[3]; a.sp_h = strides[4]; a.sp_t = strides[5];
+    a.so_b = strides[6]; a.so_h = strides[7]; a.so_t = strides[8];
+    a.B = B; a.H = H; a.head_dim = head_dim; a.side_d = side_d; a.side_t = side_t;
+    return hip_status(vs::launch_ocache_correct(a, (hipStream_t)stream));
+}
+
 const char* varsparse_strerror(int code) {
     switch (code) {
         case VARSPARSE_OK: return "ok";

@@ -74,6 +74,15 @@ struct SelMapArgs {
     int32_t* kv_idx;
 };
 
+struct OcacheArgs {
+    const __bf16* o_full;      // decision scale, full attention output
+    const __bf16* o_sparse;    // decision scale, sparse attention output
+    __bf16* o_t;               // target scale, sparse output corrected in place
+    int64_t sf_b, sf_h, sf_t, sp_b, sp_h, sp_t, so_b, so_h, so_t;
+    int32_t B, H, head_dim, side_d, side_t;
+};
+
+hipError_t launch_ocache_correct(const OcacheArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStream_t stream);
 hipError_t launch_attn_fp32(const AttnF32Args& a, int head_dim, bool dense, hipStream_t stream);
 hipError_t launch_csla_mask(const MaskArgs& a, int nqb, hipStream_t stream);

@@ -184,6 +184,26 @@ int varsparse_dense_attn_fwd(varsparse_dtype dtype, int32_t B, int32_t H, int32_
                              const void* q, const void* k, const void* v, void* o, float* lse,
                              const int64_t strides[12], float softmax_scale, void* stream);
 
+/*
+ * O_cache correction (SparVAR, ai.info summary, "Methodology in Plain
+ * English", first module: the decision scale's leftover output is cached and
+ * upsampled to correct the later sparse outputs; "Main Findings", the item on
+ * the two modules' increments).  For every (b, h), target token (y, x) and
+ * head dim c:
+ *     o_t[y, x, c] += o_full_d[y', x', c] - o_sparse_d[y', x', c],
+ *     y' = floor(y side_d / side_t), x' = floor(x side_d / side_t),
+ * with o_full_d / o_sparse_d the decision scale's full and block-sparse
+ * attention outputs and o_t the target scale's block-sparse output, updated
+ * in place (fp32 arithmetic, one rounding to bf16).
+ * All three: dev bf16 [B, H, side^2, head_dim], head dim contiguous, 16-byte
+ * aligned; strides: 9 element strides {full_b, full_h, full_t, sparse_b,
+ * sparse_h, sparse_t, t_b, t_h, t_t}, multiples of 8.  1 <= side_d <= side_t,
+ * head_dim a multiple of 8; o_t must not overlap the two decision outputs.
+ */
+int varsparse_ocache_correct(int32_t B, int32_t H, int32_t head_dim, int32_t side_d, int32_t side_t,
+                             const void* o_full_d, const void* o_sparse_d, void* o_t,
+                             const int64_t strides[9], void* stream);
+
 /* Static description of a status code. */
 const char* varsparse_strerror(int code);
 

@@ -133,3 +133,20 @@ def test_map_indices_validation():
     assert call(sel_cnt=FAKE) == _lib.EINVAL             # selection outputs come in pairs
     assert call(qd=FAKE) == _lib.EINVAL                  # scoring needs k and strides
     assert call(qd=FAKE, d=96) == _lib.EUNSUPPORTED
+
+
+def test_ocache_validation():
+    lib = _lib.lib()
+    st = (ctypes.c_int64 * 9)(*([128 * 1024, 1024 * 128, 128] * 3))
+    p = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced: validation fails first
+    call = lambda B=1, H=1, d=128, sd=32, stt=64, f=p, sp=p, o=p, strides=st: lib.varsparse_ocache_correct(
+        B, H, d, sd, stt, f, sp, o, strides, None)
+    assert call(B=0) == _lib.EINVAL
+    assert call(H=-1) == _lib.EINVAL
+    assert call(d=12) == _lib.EINVAL                 # not a multiple of 8
+    assert call(sd=0) == _lib.EINVAL
+    assert call(sd=64, stt=32) == _lib.EINVAL        # target smaller than the decision scale
+    assert call(f=None) == _lib.EINVAL
+    assert call(o=ctypes.c_void_p((1 << 20) + 8)) == _lib.EINVAL   # misaligned
+    bad = (ctypes.c_int64 * 9)(*([128 * 1024, 1024 * 128, 130] * 3))
+    assert call(strides=bad) == _lib.EINVAL          # token stride not a multiple of 8
