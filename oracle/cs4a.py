@@ -17,7 +17,9 @@ Readings taken where the pages leave a step open:
   row of scores sums to 1 (the pages say "sums"; the constant factor does not
   change any ranking);
 * selection keeps the most massive key tiles up to a cumulative mass top_p
-  (the crossing tile included).  Scores are first quantised to integers
+  (the crossing tile included); the alternative Top-K rule (the pages give a
+  Top-K ratio of about 0.2 as the stable setting, "Main Findings", decision
+  scale item) keeps the first ceil(frac * nkb) tiles of the same order.  Scores are first quantised to integers
   m = floor(score * 2^24) from their float32 value, tiles are ordered by
   (m descending, id ascending), the threshold is ceil(top_p * sum m) computed
   in IEEE double, and the shortest prefix whose sum reaches it is kept;
@@ -88,6 +90,36 @@ def top_p_select(scores_f32: np.ndarray, top_p: float):
     idx = np.full(flat.shape, -1, np.int32)
     for r in range(flat.shape[0]):
         kept = top_p_row(flat[r], top_p)
+        cnt[r] = kept.size
+        idx[r, : kept.size] = kept
+    return cnt.reshape(sc.shape[:-1]), idx.reshape(sc.shape)
+
+
+def top_k_count(nkb: int, frac: float) -> int:
+    """Tiles kept per query tile by the Top-K-fraction rule: ceil of the
+    float32 product frac * nkb (so that 0.2 of 160 is 32, not 33 as the
+    float32 value of 0.2, slightly above 0.2, would give in double), clamped
+    to [1, nkb]."""
+    k = math.ceil(float(np.float32(frac) * np.float32(nkb)))
+    return min(max(k, 1), nkb)
+
+
+def top_k_row(scores_row_f32: np.ndarray, frac: float) -> np.ndarray:
+    """Ascending ids of the top_k_count tiles first in the (m descending, id
+    ascending) order of the quantised scores."""
+    m = quantise(scores_row_f32)
+    order = sorted(range(m.size), key=lambda j: (-int(m[j]), j))
+    return np.array(sorted(order[: top_k_count(m.size, frac)]), np.int64)
+
+
+def top_k_select(scores_f32: np.ndarray, frac: float):
+    """(cnt int32 [..., nqb], idx int32 [..., nqb, nkb] ascending, -1 padded)."""
+    sc = np.asarray(scores_f32, np.float32)
+    flat = sc.reshape(-1, sc.shape[-1])
+    cnt = np.zeros(flat.shape[0], np.int32)
+    idx = np.full(flat.shape, -1, np.int32)
+    for r in range(flat.shape[0]):
+        kept = top_k_row(flat[r], frac)
         cnt[r] = kept.size
         idx[r, : kept.size] = kept
     return cnt.reshape(sc.shape[:-1]), idx.reshape(sc.shape)

@@ -160,3 +160,38 @@ def test_map_monotone_and_sinks():
         s1, s2 = set(i1[q, : c1[q]]), set(i2[q, : c2[q]])
         assert s1 <= s2
         assert {0, 1, 2, 3, 4} <= s1
+
+
+# ---- Top-K-fraction selector
+
+
+def test_top_k_count():
+    from oracle import cs4a as OC
+    assert OC.top_k_count(47, 0.2) == 10            # ceil(9.4)
+    assert OC.top_k_count(160, 0.2) == 32            # float32 product 32.0 exactly
+    assert OC.top_k_count(5, 0.0001) == 1            # at least one tile
+    assert OC.top_k_count(5, 1.0) == 5
+
+
+def test_top_k_full_fraction_keeps_all_and_argmax():
+    from oracle import cs4a as OC
+    rng = np.random.default_rng(11)
+    row = rng.random(31).astype(np.float32)
+    assert np.array_equal(OC.top_k_row(row, 1.0), np.arange(31))
+    one = OC.top_k_row(row, 1e-6)
+    assert one.tolist() == [int(np.argmax(OC.quantise(row)))]
+
+
+def test_top_k_ties_go_to_lower_ids_and_set_is_a_top_set():
+    from oracle import cs4a as OC
+    row = np.array([0.1, 0.3, 0.3, 0.05, 0.3, 0.25], np.float32)
+    # three equal maxima; keep 2 -> the two lowest ids among them
+    assert OC.top_k_row(row, 2 / 6).tolist() == [1, 2]
+    rng = np.random.default_rng(12)
+    for _ in range(20):
+        r = rng.random(40).astype(np.float32)
+        kept = OC.top_k_row(r, 0.2)
+        m = OC.quantise(r)
+        rest = np.setdiff1d(np.arange(40), kept)
+        assert m[kept].min() >= m[rest].max()
+        assert kept.size == OC.top_k_count(40, 0.2)
