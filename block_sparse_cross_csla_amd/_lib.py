@@ -21,6 +21,7 @@ EXPORTS = (
     "varsparse_geom_counts",
     "varsparse_build_mask",
     "varsparse_map_indices",
+    "varsparse_map_indices_topk",
     "varsparse_attn_fwd",
     "varsparse_dense_attn_fwd",
     "varsparse_ocache_correct",
@@ -53,13 +54,14 @@ def _load():
     lib.varsparse_build_mask.argtypes = [PG, I32, I32, PI32, I32, P, P, P, P]
     lib.varsparse_map_indices.argtypes = [PG, I32, I32, I32, F32, I32, I32, I32, I32,
                                           P, PI64, P, PI64, F32, P, P, P, P, P, P]
+    lib.varsparse_map_indices_topk.argtypes = lib.varsparse_map_indices.argtypes
     lib.varsparse_attn_fwd.argtypes = [PG, I32, I32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32, P]
     lib.varsparse_dense_attn_fwd.argtypes = [I32, I32, I32, I32, I64, I64, P, P, P, P, P, PI64, F32, P]
     lib.varsparse_ocache_correct.argtypes = [I32, I32, I32, I32, I32, P, P, P, PI64, P]
     lib.varsparse_strerror.argtypes = [ctypes.c_int]
     lib.varsparse_strerror.restype = ctypes.c_char_p
     lib.varsparse_last_hip_error.argtypes = []
-    for name in EXPORTS[:6]:
+    for name in EXPORTS[:7]:
         getattr(lib, name).restype = ctypes.c_int
     lib.varsparse_last_hip_error.restype = ctypes.c_int
     return lib
@@ -144,9 +146,11 @@ def build_mask(sides, tile: int, q_scale: int, n_sink: int, radius=None, budget:
 
 
 def map_indices(sides, tile: int, d_scale: int, t_scale: int, n_sink: int, top_p: float,
-                q_d=None, k=None, softmax_scale=None, scores=None, want_selection=False, out=None, stream=None):
+                q_d=None, k=None, softmax_scale=None, scores=None, want_selection=False, out=None, stream=None,
+                top_k=None):
     """CS4A: scores (computed when q_d is given, else taken from ``scores``),
-    selection and per-(b,h) target lists.  Returns (scores, sel_cnt, sel_idx, kv_cnt, kv_idx)."""
+    selection and per-(b,h) target lists.  Returns (scores, sel_cnt, sel_idx, kv_cnt, kv_idx).
+    With ``top_k`` (a fraction in (0, 1]) the Top-K rule replaces top-p."""
     if q_d is not None:
         B, H, _, d = q_d.shape
         device = q_d.device
@@ -177,10 +181,12 @@ def map_indices(sides, tile: int, d_scale: int, t_scale: int, n_sink: int, top_p
         dt = _dtype_code(q_d)
     else:
         scale, qs, ks, dt = 1.0, None, None, BF16
-    _check(_LIB.varsparse_map_indices(ctypes.byref(g), d_scale, t_scale, n_sink, float(top_p), dt, B, H, d,
-                                      _ptr(q_d), qs, _ptr(k), ks, float(scale), _ptr(scores),
-                                      _ptr(sel_cnt), _ptr(sel_idx), _ptr(kv_cnt), _ptr(kv_idx), _stream(stream)),
-           "varsparse_map_indices")
+    fn, name, param = _LIB.varsparse_map_indices, "varsparse_map_indices", top_p
+    if top_k is not None:
+        fn, name, param = _LIB.varsparse_map_indices_topk, "varsparse_map_indices_topk", top_k
+    _check(fn(ctypes.byref(g), d_scale, t_scale, n_sink, float(param), dt, B, H, d,
+              _ptr(q_d), qs, _ptr(k), ks, float(scale), _ptr(scores),
+              _ptr(sel_cnt), _ptr(sel_idx), _ptr(kv_cnt), _ptr(kv_idx), _stream(stream)), name)
     return scores, sel_cnt, sel_idx, kv_cnt, kv_idx
 
 

@@ -94,12 +94,17 @@ int varsparse_build_mask(const varsparse_geom* geom, int32_t q_scale, int32_t n_
     return hip_status(vs::launch_csla_mask(a, nqb, (hipStream_t)stream));
 }
 
-int varsparse_map_indices(const varsparse_geom* geom, int32_t d_scale, int32_t t_scale, int32_t n_sink,
-                          float top_p, varsparse_dtype dtype, int32_t B, int32_t H, int32_t head_dim,
-                          const void* q_d, const int64_t q_strides[3], const void* k,
-                          const int64_t k_strides[3], float softmax_scale, float* scores,
-                          int32_t* sel_cnt, int32_t* sel_idx, int32_t* kv_cnt, int32_t* kv_idx,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+
+// CS4A with selection rule 0 (top-p, param = p) or 1 (Top-K fraction).
+int map_indices_impl(const varsparse_geom* geom, int32_t d_scale, int32_t t_scale, int32_t n_sink, int rule,
+                     float top_p, varsparse_dtype dtype, int32_t B, int32_t H, int32_t head_dim,
+                     const void* q_d, const int64_t q_strides[3], const void* k,
+                     const int64_t k_strides[3], float softmax_scale, float* scores,
+                     int32_t* sel_cnt, int32_t* sel_idx, int32_t* kv_cnt, int32_t* kv_idx,
+                     void* stream) {
     int rc = check_geom(geom);
     if (rc) return rc;
     if (d_scale < 0 || t_scale < d_scale || t_scale >= geom->n_scales) return VARSPARSE_EINVAL;
@@ -150,6 +155,9 @@ int varsparse_map_indices(const varsparse_geom* geom, int32_t d_scale, int32_t t
     m.nqbT = nqbT;
     m.nkbT = nkbT;
     m.words = words;
+    m.rule = rule;
+    // Top-K: ceil of the float32 product frac * nkb_D, clamped to [1, nkb_D]
+    m.k_keep = std::min(std::max((int)ceilf(top_p * (float)nkbD), 1), nkbD);
     m.top_p = (double)top_p;
     m.scores = scores;
     m.sel_cnt = sel_cnt;
@@ -157,6 +165,30 @@ int varsparse_map_indices(const varsparse_geom* geom, int32_t d_scale, int32_t t
     m.kv_cnt = kv_cnt;
     m.kv_idx = kv_idx;
     return hip_status(vs::launch_cs4a_select_map(m, B * H, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int varsparse_map_indices(const varsparse_geom* geom, int32_t d_scale, int32_t t_scale, int32_t n_sink,
+                          float top_p, varsparse_dtype dtype, int32_t B, int32_t H, int32_t head_dim,
+                          const void* q_d, const int64_t q_strides[3], const void* k,
+                          const int64_t k_strides[3], float softmax_scale, float* scores,
+                          int32_t* sel_cnt, int32_t* sel_idx, int32_t* kv_cnt, int32_t* kv_idx,
+                          void* stream) {
+    return map_indices_impl(geom, d_scale, t_scale, n_sink, 0, top_p, dtype, B, H, head_dim, q_d, q_strides, k,
+                            k_strides, softmax_scale, scores, sel_cnt, sel_idx, kv_cnt, kv_idx, stream);
+}
+
+int varsparse_map_indices_topk(const varsparse_geom* geom, int32_t d_scale, int32_t t_scale, int32_t n_sink,
+                               float top_k_frac, varsparse_dtype dtype, int32_t B, int32_t H, int32_t head_dim,
+                               const void* q_d, const int64_t q_strides[3], const void* k,
+                               const int64_t k_strides[3], float softmax_scale, float* scores,
+                               int32_t* sel_cnt, int32_t* sel_idx, int32_t* kv_cnt, int32_t* kv_idx,
+                               void* stream) {
+    return map_indices_impl(geom, d_scale, t_scale, n_sink, 1, top_k_frac, dtype, B, H, head_dim, q_d, q_strides,
+                            k, k_strides, softmax_scale, scores, sel_cnt, sel_idx, kv_cnt, kv_idx, stream);
 }
 
 int varsparse_attn_fwd(const varsparse_geom* geom, int32_t q_scale, varsparse_dtype dtype, int32_t B, int32_t H,

@@ -13,8 +13,8 @@
 // kernel.  Reductions run in a fixed order: scores are bit-reproducible.
 //
 // cs4a_select_map_kernel: one wave per (batch, head, target query tile).
-// Top-p on integer-quantised scores (exact, associative) of the parent
-// decision tile, kept as a bitset in registers, then the target-scale lists: parent tile by floor scaling, tiles below the
+// Top-p (or Top-K) on integer-quantised scores (exact, associative) of the
+// parent decision tile, kept as a bitset in registers, then the target-scale lists: parent tile by floor scaling, tiles below the
 // decision scale copied, decision-scale tiles expanded to their footprint on
 // every scale from D to the target, sink tiles added.
 #include "kernel_args.h"
@@ -253,12 +253,14 @@ __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a
         if (64 * w4 < nkbD) {
             if (j < nkbD) {
                 const int64_t mj = mq[wave][j];
+                // mass (top-p) or number (Top-K) of the tiles ordered before j
+                const bool by_mass = a.rule == 0;
                 int64_t before = 0;
                 for (int i = 0; i < nkbD; ++i) {
                     const int64_t mi = mq[wave][i];
-                    before += (mi > mj || (mi == mj && i < j)) ? mi : 0;
+                    before += (mi > mj || (mi == mj && i < j)) ? (by_mass ? mi : 1) : 0;
                 }
-                keep = (double)before < thr;
+                keep = by_mass ? (double)before < thr : before < a.k_keep;
             }
             sel[w4] = __ballot(keep);
         }

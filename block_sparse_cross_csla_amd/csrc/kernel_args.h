@@ -66,6 +66,8 @@ struct ScoreArgs {
 struct SelMapArgs {
     DevGeom g;   // scales 0..T
     int32_t d_scale, t_scale, n_sink, nqbD, nkbD, nqbT, nkbT, words;
+    int32_t rule;     // 0: top-p (top_p), 1: Top-K fraction (k_keep tiles)
+    int32_t k_keep;
     double top_p;
     const float* scores;
     int32_t* sel_cnt;

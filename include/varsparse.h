@@ -148,6 +148,24 @@ int varsparse_map_indices(const varsparse_geom* geom, int32_t d_scale, int32_t t
                           int32_t* kv_cnt, int32_t* kv_idx, void* stream);
 
 /*
+ * CS4A with the Top-K-fraction selection rule (SparVAR, ai.info summary,
+ * "Main Findings", decision-scale item: a Top-K ratio of about 0.2 is the
+ * stable setting; "Methodology in Plain English", first module: a Top-K
+ * operation picks the key blocks).  Identical to varsparse_map_indices except
+ * for the selection: per decision query tile the first
+ * k = min(max(ceil(top_k_frac * nkb_D), 1), nkb_D) key tiles (the product in
+ * IEEE single precision) of the order (m descending, id ascending) are kept.
+ * 0 < top_k_frac <= 1.
+ */
+int varsparse_map_indices_topk(const varsparse_geom* geom, int32_t d_scale, int32_t t_scale,
+                               int32_t n_sink, float top_k_frac, varsparse_dtype dtype,
+                               int32_t B, int32_t H, int32_t head_dim,
+                               const void* q_d, const int64_t q_strides[3],
+                               const void* k, const int64_t k_strides[3], float softmax_scale,
+                               float* scores, int32_t* sel_cnt, int32_t* sel_idx,
+                               int32_t* kv_cnt, int32_t* kv_idx, void* stream);
+
+/*
  * Block-sparse attention of query scale q_scale over its cache (SparVAR,
  * ai.info summary, "Key Contributions" item 3 and "Main Findings", the
  * block-wise sparse kernel).  For every query of tile Q:

@@ -133,3 +133,27 @@ def test_full_size_cs4a_lists():
         assert (lists[T][1].cpu().numpy() == mi).all()
     ref = OC.block_scores(q_d[1:, 14:], k[1:, 14:], w.sides, D, w.tile, 1 / math.sqrt(w.d))
     assert np.abs(s[1:, 14:] - ref).max() <= SCORE_TOL
+
+
+@pytest.mark.parametrize("frac", [0.2, 0.05, 1.0])
+def test_top_k_selection_and_mapping_bit_exact(cs4a_run, frac):
+    """The Top-K-fraction rule on the GPU's own scores: selection and every
+    target's lists equal the oracle's (integer decisions on the same float32
+    values), including the degenerate fractions (one tile, every tile)."""
+    vs = _vs()
+    r = cs4a_run
+    w = r["w"]
+    scores = torch.from_numpy(r["scores"]).cuda()
+    gpu = {}
+    for T in W.CS4A_TARGETS:
+        _, sc, si, kc, ki = vs.map_indices(w.sides, w.tile, r["D"], T, w.n_sink, 0.9, scores=scores,
+                                           want_selection=True, top_k=frac)
+        gpu[T] = (sc.cpu().numpy(), si.cpu().numpy(), kc.cpu().numpy(), ki.cpu().numpy())
+    torch.cuda.synchronize()
+    cnt, idx = OC.top_k_select(r["scores"], frac)
+    assert (cnt == OC.top_k_count(r["scores"].shape[-1], frac)).all()
+    for T in W.CS4A_TARGETS:
+        sc, si, kc, ki = gpu[T]
+        assert (sc == cnt).all() and (si == idx).all()
+        mc, mi = OC.map_indices(cnt, idx, w.sides, r["D"], T, w.tile, w.n_sink)
+        assert (kc == mc).all() and (ki == mi).all()
