@@ -90,3 +90,31 @@ def dense_attention(q, k, v, softmax_scale: float, q_rows=None, bh=None):
         o[b, h, rows] = oi
         lse[b, h, rows] = li
     return o, lse
+
+
+def token_masked_attention(q, k, v, sides, q_scale: int, t: int, n_sink: int, radius, softmax_scale: float,
+                           q_tiles=None, bh=None):
+    """Attention under the token-level CSLA mask itself (SparVAR, ai.info
+    summary, "Key Contributions" item 3: the naive token-wise sparse attention
+    baseline the block kernel is compared with; "Methodology in Plain
+    English", second module: a key is kept iff its scale is a sink or it lies
+    in the per-scale window around the query's projection).  The same result
+    as block-sparse attention over the CSLA tiles with the token rule applied
+    inside them (every kept token pair lies in a kept tile).  q [B,H,side^2,d],
+    k/v [B,H,Nk,d]; optional query-tile / (b, h) subsets; other rows NaN."""
+    from . import csla
+    B, Hh, nq, d = q.shape
+    qts = G.query_tiles(sides, q_scale, t)
+    sel = range(len(qts)) if q_tiles is None else q_tiles
+    o = np.full((B, Hh, nq, d), np.nan)
+    lse = np.full((B, Hh, nq), np.nan)
+    pairs = bh if bh is not None else [(b, h) for b in range(B) for h in range(Hh)]
+    for r in sel:
+        qt = qts[r]
+        rows = qt.tokens()
+        keep = csla.token_mask_for_query_tile(sides, q_scale, t, n_sink, radius, qt)
+        for (b, h) in pairs:
+            oi, li = softmax_attention(q[b, h, rows], k[b, h], v[b, h], keep, softmax_scale)
+            o[b, h, rows] = oi
+            lse[b, h, rows] = li
+    return o, lse

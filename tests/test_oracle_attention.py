@@ -96,3 +96,64 @@ def test_scale_matters():
     o2, _ = A.softmax_attention(q, k, v, np.ones((5, 9), bool), 1.0)
     assert np.abs(o1 - o2).max() > 1e-3
     assert np.abs(o1 - _sdpa(q, k, v, 0.1)).max() < 1e-12
+
+
+# ---- token-level CSLA mask
+
+
+def _tiny_inputs(seed=5):
+    from varsparse_inputs import TINY_SIDES
+    rng = np.random.default_rng(seed)
+    sides = list(TINY_SIDES)
+    nk = sum(s * s for s in sides)
+    q = rng.normal(size=(1, 1, sides[-1] ** 2, 16))
+    k = rng.normal(size=(1, 1, nk, 16))
+    v = rng.normal(size=(1, 1, nk, 16))
+    return sides, q, k, v
+
+
+def test_token_masked_wide_window_is_dense():
+    from oracle import attention as OA
+    sides, q, k, v = _tiny_inputs()
+    qs = len(sides) - 1
+    o, l = OA.token_masked_attention(q, k, v, sides, qs, 4, 0, [max(sides)] * len(sides), 0.25)
+    ro, rl = OA.dense_attention(q, k, v, 0.25)
+    np.testing.assert_allclose(o, ro, atol=1e-12)
+    np.testing.assert_allclose(l, rl, atol=1e-12)
+
+
+def test_token_masked_sinks_only_is_attention_over_the_sink_tokens():
+    from oracle import attention as OA
+    sides, q, k, v = _tiny_inputs(6)
+    qs, n_sink = len(sides) - 1, 2
+    o, l = OA.token_masked_attention(q, k, v, sides, qs, 4, n_sink, [-1] * len(sides), 0.25)
+    ns = sum(s * s for s in sides[:n_sink])
+    ro, rl = OA.dense_attention(q, k[:, :, :ns], v[:, :, :ns], 0.25)
+    np.testing.assert_allclose(o, ro, atol=1e-12)
+    np.testing.assert_allclose(l, rl, atol=1e-12)
+
+
+def test_token_masked_matches_per_query_gather():
+    """Second route: per query, gather the kept keys by the window rule
+    written out with explicit loops and run textbook attention on them."""
+    from oracle import attention as OA
+    sides, q, k, v = _tiny_inputs(7)
+    qs, n_sink, radius = len(sides) - 1, 2, [1, 1, 1, 0, 1]
+    o, l = OA.token_masked_attention(q, k, v, sides, qs, 4, n_sink, radius, 0.3)
+    H = sides[qs]
+    offs = np.cumsum([0] + [s * s for s in sides])
+    for y in range(H):
+        for x in range(H):
+            keys = []
+            for s, h in enumerate(sides[: qs + 1]):
+                py, px = (y * h) // H, (x * h) // H
+                for yy in range(h):
+                    for xx in range(h):
+                        if s < n_sink or (radius[s] >= 0 and abs(yy - py) <= radius[s] and abs(xx - px) <= radius[s]):
+                            keys.append(offs[s] + yy * h + xx)
+            qi = q[0, 0, y * H + x]
+            sc = np.array([qi @ k[0, 0, j] for j in keys]) * 0.3
+            p = np.exp(sc - sc.max())
+            ref = (p[:, None] * v[0, 0, keys]).sum(0) / p.sum()
+            np.testing.assert_allclose(o[0, 0, y * H + x], ref, atol=1e-12)
+            np.testing.assert_allclose(l[0, 0, y * H + x], sc.max() + np.log(p.sum()), atol=1e-12)
