@@ -165,6 +165,29 @@ def main():
     dense_ms = float(np.mean([de[i][0].elapsed_time(de[i][1]) for i in range(nd)]))
     print(f"[bench] dense done: {dense_ms:.4f} ms", file=sys.stderr, flush=True)
 
+    # token-level CSLA on the same tensors: the token-masked dense baseline
+    # (every key tile, the token rule applied) and token-exact block-sparse
+    # attention (the CSLA tiles, the token rule inside them)
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for e in evs:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+
+    tok_dense_ms = timed(lambda: vs.attn_fwd_token(q, k, v, w.sides, w.tile, w.q_scale, w.n_sink, w.radii,
+                                                   softmax_scale=scale, out=od, lse=lsed, stream=stream), nd)
+    tok_sparse_ms = timed(lambda: vs.attn_fwd_token(q, k, v, w.sides, w.tile, w.q_scale, w.n_sink, w.radii, kv_cnt, kv_idx,
+                                                    softmax_scale=scale, out=od, lse=lsed, stream=stream),
+                          args.steps)
+    print(f"[bench] token-wise done: dense {tok_dense_ms:.4f} ms, exact sparse {tok_sparse_ms:.4f} ms",
+          file=sys.stderr, flush=True)
+
     result = {
         "metric": "last-scale sparse-attn effective TFLOP/s + speedup vs dense attn, 1 MI355X",
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -188,10 +211,14 @@ def main():
         "dense_kernel_ms": dense_ms,
         "dense_tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
         "block_sparsity": {"count": float(count_sparsity), "flop": float(flop_sparsity)},
+        "token_wise": {"token_masked_dense_ms": tok_dense_ms, "token_exact_sparse_ms": tok_sparse_ms,
+                       "block_sparse_ms": attn_ms, "block_vs_token_masked_dense": tok_dense_ms / attn_ms,
+                       "token_exact_vs_token_masked_dense": tok_dense_ms / tok_sparse_ms,
+                       "pages_block_vs_token_wise": 15.26},
         "roofline": {"bound": "mfma", "achieved": flops / (attn_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                      "traffic": TRAFFIC["bytes"] if kernel_sources_sha256() == TRAFFIC["sources_sha256"] else None,
-                     "traffic_unit": "bytes per launch", "kernel": "attn_fwd_bf16_kernel<128,false>",
+                     "traffic_unit": "bytes per launch", "kernel": "attn_fwd_bf16_kernel<128,false,false>",
                      "flop_per_launch": flops},
     }
 

@@ -88,7 +88,7 @@ __device__ __forceinline__ int build_table(Walk& w, const DevGeom& g, uint2* tab
     while (w.j < w.cnt && kTableCap - n >= 128) {
         const int e = w.j + lane;
         const bool valid = e < w.cnt;
-        int id = valid ? w.idx[e] : 0;
+        int id = valid ? (w.idx != nullptr ? w.idx[e] : e) : 0;   // no list: every tile in order
         id = min(max(id, 0), g.tile_base[g.n_scales] - 1);
         int tb = 0, side = g.side[0], off = 0, nb = g.nb[0];
         for (int s = 1; s < g.n_scales; ++s) {
@@ -214,7 +214,8 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 // next to their uses.
 template <int D>
 __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __restrict__ kst,
-                                             const char* __restrict__ vst, const Chunk& cc, float c, int lane) {
+                                             const char* __restrict__ vst, const Chunk& cc, float c, int lane,
+                                             uint32_t tokmask = 0xffffu) {
     constexpr int KSTEPS = D / 16;
     constexpr int MBLK = D / 32;
     constexpr int ROWB = D * 2;
@@ -258,6 +259,12 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    // keys outside the token-level mask (token-exact mode) -> -inf
+    if (tokmask != 0xffffu) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (!((tokmask >> i) & 1u)) sacc[i] = -INFINITY;
+    }
     // padding keys of partial chunks -> -inf (value i sits at row i/4, column 4g + i%4)
     if (!cc.full) {
 #pragma unroll
@@ -298,7 +305,43 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
             st.oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[mb][t], pt[t], st.oacc[mb], 0, 0, 0);
 }
 
-template <int D, bool DENSE>
+// floor(num / den) for 0 <= num < 2^24, den >= 1 (float estimate, one correction each way)
+__device__ __forceinline__ int div_floor(int num, int den) {
+    int q = (int)((float)num / (float)den);
+    q -= (q * den > num);
+    q += ((q + 1) * den <= num);
+    return q;
+}
+
+// Token-level CSLA keep bits of a tile-half chunk for this lane (value i at
+// key row i/4, column 4g + i%4 of the chunk): a key of scale s at (y', x') is
+// kept iff s is a sink scale, or radius[s] >= 0 and |y' - floor(qy h_s / H)|
+// and |x' - floor(qx h_s / H)| are both <= radius[s] (SparVAR, ai.info
+// summary, "Methodology in Plain English", second module).  Chunks of sink
+// scales keep every key.
+__device__ __forceinline__ uint32_t csla_token_bits(const AttnArgs& a, int32_t base, int qy, int qx, int g) {
+    if (base < a.g.tok_off[a.n_sink]) return 0xffffu;
+    int s = a.n_sink;
+    while (s + 1 < a.g.n_scales && a.g.tok_off[s + 1] <= base) ++s;
+    const int r = a.radius[s];
+    if (r < 0) return 0u;
+    const int side = a.g.side[s], local = base - a.g.tok_off[s];
+    const int y0 = __builtin_amdgcn_readfirstlane(div_floor(local, side));
+    const int x0 = local - y0 * side;
+    const int py = div_floor(qy * side, a.q_side), px = div_floor(qx * side, a.q_side);
+    uint32_t rows = 0u, cols = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        rows |= (uint32_t)(abs(y0 + k - py) <= r) << k;
+        cols |= (uint32_t)(abs(x0 + 4 * g + k - px) <= r) << k;
+    }
+    uint32_t bits = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) bits |= ((rows >> k) & 1u) ? (cols << (4 * k)) : 0u;
+    return bits;
+}
+
+template <int D, bool DENSE, bool TOKEN>
 __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a) {
     constexpr int KSTEPS = D / 16;
     constexpr int MBLK = D / 32;
@@ -317,6 +360,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     // ---- the query this lane holds (column n of the wave's 32 queries)
     int64_t tok;
     bool qvalid = true;
+    int qy = 0, qx = 0;   // the query's grid coordinates (token mode)
     if (DENSE) {
         tok = 64 * (int64_t)qt + 32 * wave + n;
         qvalid = tok < a.nq;
@@ -324,7 +368,9 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     } else {
         const int nbq = a.q_side >> 3;
         const int ti = qt / nbq, tj = qt - ti * nbq;
-        tok = (int64_t)(8 * ti + 4 * wave + (n >> 3)) * a.q_side + 8 * tj + (n & 7);
+        qy = 8 * ti + 4 * wave + (n >> 3);
+        qx = 8 * tj + (n & 7);
+        tok = (int64_t)qy * a.q_side + qx;
     }
     const __bf16* kh = a.k + b * a.sk_b + h * a.sk_h;
     const __bf16* vh = a.v + b * a.sv_b + h * a.sv_h;
@@ -346,13 +392,18 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         nch = (w.cend + 31) >> 5;
     } else {
         const int64_t row = (a.per_head ? (int64_t)bh * a.nqb : 0) + qt;
-        w.cnt = a.kv_cnt[row];
-        w.idx = a.kv_idx + row * a.nkb;
+        if (a.kv_cnt != nullptr) {
+            w.cnt = a.kv_cnt[row];
+            w.idx = a.kv_idx + row * a.nkb;
+        } else {   // token mode without a list: every key tile
+            w.cnt = a.nkb;
+            w.idx = nullptr;
+        }
         // leading run of tiles 0,1,2,...: whole scales kept from the start form
         // one contiguous token range
         int p = 0;
         for (;;) {
-            const int v = (p + lane < w.cnt) ? w.idx[p + lane] : -1;
+            const int v = (p + lane < w.cnt) ? (w.idx != nullptr ? w.idx[p + lane] : p + lane) : -1;
             const uint64_t off = __ballot(v != p + lane);
             if (off) {
                 p += __builtin_ctzll(off);
@@ -362,6 +413,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         }
         int s = 0;
         while (s < a.g.n_scales && a.g.tile_base[s + 1] <= p) ++s;
+        if (TOKEN) s = min(s, a.n_sink);   // only sink scales skip the token test
         w.cnext = 0;
         w.cend = a.g.tok_off[s];
         w.j = a.g.tile_base[s];
@@ -379,7 +431,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     for (int s = 0; s < KSTEPS; ++s) st.qreg[s] = *(const bf16x8*)(qp + 16 * s + 8 * g);
 #pragma unroll
     for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] = (f32x16)0.0f;
-    st.m_run = -INFINITY;
+    st.m_run = -1e30f;   // finite: a fully masked chunk gives P = 0, not NaN
     st.l_run = 0.0f;
     LoadPlan<D> plan;
     make_plan<D>(plan, wave, lane, a.sk_t, a.sv_t);
@@ -420,7 +472,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
                 nxt = desc(ci + 1);
                 load_chunk<D>(plan, kh, vh, krb, vrb, nxt, lds0 + 2 * STAGE, lds0 + 3 * STAGE, wave, lane);
             }
-            attend_chunk<D>(st, sm, sm + STAGE, cur, c, lane);
+            attend_chunk<D>(st, sm, sm + STAGE, cur, c, lane, TOKEN ? csla_token_bits(a, cur.base, qy, qx, g) : 0xffffu);
             if (ci + 1 >= nch) break;
             cur = nxt;
             wait_vmcnt(0);
@@ -429,7 +481,8 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
                 nxt = desc(ci + 2);
                 load_chunk<D>(plan, kh, vh, krb, vrb, nxt, lds0, lds0 + STAGE, wave, lane);
             }
-            attend_chunk<D>(st, sm + 2 * STAGE, sm + 3 * STAGE, cur, c, lane);
+            attend_chunk<D>(st, sm + 2 * STAGE, sm + 3 * STAGE, cur, c, lane,
+                            TOKEN ? csla_token_bits(a, cur.base, qy, qx, g) : 0xffffu);
             cur = nxt;
         }
         if (DENSE) break;
@@ -470,12 +523,15 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStre
     const int64_t nqt = dense ? (a.nq + 63) / 64 : a.nqb;
     const int64_t blocks = nqt * a.B * a.H;
     dim3 grid((unsigned)blocks), block(128);
+    const bool token = a.token != 0 && !dense;
     if (head_dim == 128) {
-        if (dense) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
+        if (dense) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true, false>), grid, block, 0, stream, a);
+        else if (token) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false, false>), grid, block, 0, stream, a);
     } else {
-        if (dense) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
+        if (dense) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true, false>), grid, block, 0, stream, a);
+        else if (token) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -21,6 +21,9 @@ struct AttnArgs {
     int32_t nqb, nkb;
     int32_t q_side;
     DevGeom g;
+    // token-exact mode (CSLA token mask inside the kept tiles; no list = every tile)
+    int32_t token, n_sink;
+    int32_t radius[kMaxScales];
     // dense walk
     int64_t nq, nk;
 };

@@ -191,6 +191,29 @@ int varsparse_attn_fwd(const varsparse_geom* geom, int32_t q_scale, varsparse_dt
                        void* stream);
 
 /*
+ * Token-exact CSLA attention (SparVAR, ai.info summary, "Methodology in Plain
+ * English", second module: the token-level sink + window mask; "Key
+ * Contributions" item 3: the naive token-wise sparse attention baseline).
+ * For every query of tile Q: softmax over the keys the token rule keeps
+ * (scale s < n_sink, or radius[s] >= 0 and |y' - floor(y h/H)| <= radius[s]
+ * and |x' - floor(x h/H)| <= radius[s]), times V, and lse as in
+ * varsparse_attn_fwd; a query keeping no key gets O = 0 and lse = -inf.
+ * With lists (kv_cnt, kv_idx as in varsparse_attn_fwd, e.g. the CSLA block
+ * mask of the same n_sink and radius) only the listed tiles are walked and the
+ * token rule is applied inside them; the result is the same as long as every
+ * kept token pair lies in a listed tile.  With kv_cnt = kv_idx = NULL every key
+ * tile is walked: the token-masked dense baseline.
+ * radius: host array of q_scale + 1 entries.  bf16, head_dim in {64, 128},
+ * tile == 8; layouts and strides as varsparse_attn_fwd.
+ */
+int varsparse_attn_fwd_token(const varsparse_geom* geom, int32_t q_scale, int32_t n_sink,
+                             const int32_t* radius, int32_t B, int32_t H, int32_t head_dim,
+                             const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int64_t strides[12], float softmax_scale,
+                             const int32_t* kv_cnt, const int32_t* kv_idx, int32_t lists_per_head,
+                             void* stream);
+
+/*
  * Dense attention written with the same tile engine, the comparator the
  * pages measure the sparse kernel against ("Main Findings": the block-wise
  * kernel vs dense FlashAttention on the last scale).  Every query attends to
