@@ -18,9 +18,11 @@ csla       the CSLA token mask (sink + cross-scale locality window), its block
            aggregation, the per-row tile budget variant, and index lists
 cs4a       decision-scale block scores, top-p selection, index mapping
 attention  masked softmax attention (mask applied token-wise as -inf)
+ocache     the decision-scale residual, upsampled onto a later scale's output
+schedule   the per-scale loop with both modules and the window schedule
 
 Every function is pinned by ``tests/test_oracle_*.py`` against something other
 than itself: library routines, closed forms, invariants, brute force on tiny
 inputs and hand-derived fixtures under ``tests/golden/``.
 """
-from . import geometry, csla, cs4a, attention  # noqa: F401
+from . import geometry, csla, cs4a, attention, ocache, schedule  # noqa: F401
