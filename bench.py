@@ -233,6 +233,10 @@ def main():
         result["cs4a"] = bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev)
         print("[bench] cs4a done", file=sys.stderr, flush=True)
 
+    if not args.no_cs4a:
+        result["scale_loop"] = bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev)
+        print("[bench] scale loop done", file=sys.stderr, flush=True)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q_np, k_np, v_np, cnt_h, idx_h, sizes, round_bf16, args.cpu_seconds)
         print("[bench] cpu baseline done", file=sys.stderr, flush=True)
@@ -340,6 +344,97 @@ def bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev):
                        "correct_side64_bytes": corr_bytes,
                        "correct_side64_gbps": corr_bytes / (res["correct_last"] * 1e-3) / 1e9,
                        "hbm_peak_gbps": 8000.0}}
+
+
+def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
+    """One generation step of attention over all 13 query scales of the 2B
+    schedule: dense below the decision scale (side 32); at it, full attention,
+    scores + selection and block-sparse attention over its own selection; at
+    sides 40/48/64, CS4A mapping joined (union) with the CSLA window lists of
+    windows 3/5/7, block-sparse attention and the O_cache correction.
+    Compared with dense attention at every scale."""
+    w = W.CS4A
+    D = W.CS4A_DECISION
+    windows = (3, 5, 7)
+    n = len(w.sides)
+    f = SpatialField(w.seed, w.wid, w.B, w.H, w.d)
+    k_np, v_np = f.keys_values(w.sides, w.n_sink)
+    k, v = to_dev(k_np), to_dev(v_np)
+    qs = [to_dev(f.queries(s)) for s in w.sides]
+    outs = [torch.empty_like(x) for x in qs]
+    nks = [vs.geom_counts(w.sides, w.tile, s)[3] for s in range(n)]
+    scale = 1.0 / math.sqrt(w.d)
+    nqb_d, nkb_d = vs.geom_counts(w.sides, w.tile, D)[:2]
+    scores = torch.empty(w.B, w.H, nqb_d, nkb_d, dtype=torch.float32, device=dev)
+    lists_d = (torch.empty(w.B, w.H, nqb_d, dtype=torch.int32, device=dev),
+               torch.empty(w.B, w.H, nqb_d, nkb_d, dtype=torch.int32, device=dev))
+    o_sparse_d = torch.empty_like(qs[D])
+    bufs = {}
+    for T in W.CS4A_TARGETS:
+        nqb, nkb = vs.geom_counts(w.sides, w.tile, T)[:2]
+        mk = lambda *lead: (torch.empty(*lead, nqb, dtype=torch.int32, device=dev),
+                            torch.empty(*lead, nqb, nkb, dtype=torch.int32, device=dev))
+        bufs[T] = (mk(w.B, w.H), mk(), mk(w.B, w.H), vs.window_radius(n, T, windows))
+
+    def dense_at(s):
+        vs.dense_attn_fwd(qs[s], k[:, :, : nks[s]], v[:, :, : nks[s]], softmax_scale=scale, out=outs[s],
+                          want_lse=False, stream=stream)
+
+    def loop_step():
+        for s in range(D + 1):
+            dense_at(s)
+        vs.map_indices(w.sides, w.tile, D, D, w.n_sink, W.CS4A_TOP_P, q_d=qs[D], k=k, scores=scores, out=lists_d,
+                       stream=stream)
+        vs.attn_fwd(qs[D], k[:, :, : nks[D]], v[:, :, : nks[D]], w.sides, w.tile, D, *lists_d, softmax_scale=scale,
+                    out=o_sparse_d, want_lse=False, stream=stream)
+        for T in W.CS4A_TARGETS:
+            mapped, window, joined, radius = bufs[T]
+            vs.map_indices(w.sides, w.tile, D, T, w.n_sink, W.CS4A_TOP_P, scores=scores, out=mapped, stream=stream)
+            vs.build_mask(w.sides, w.tile, T, w.n_sink, radius=radius, out=(*window, None), stream=stream)
+            vs.join_lists(*mapped, *window, join="union", out=joined, stream=stream)
+            vs.attn_fwd(qs[T], k[:, :, : nks[T]], v[:, :, : nks[T]], w.sides, w.tile, T, *joined,
+                        softmax_scale=scale, out=outs[T], want_lse=False, stream=stream)
+            vs.ocache_correct(outs[D], o_sparse_d, outs[T], w.sides[D], w.sides[T], stream=stream)
+
+    def dense_step():
+        for s in range(n):
+            dense_at(s)
+
+    def below_d():
+        for s in range(D):
+            dense_at(s)
+
+    reps = max(5, args.steps // 2)
+    res = {}
+    for name, fn in (("loop", loop_step), ("dense", dense_step), ("below_d", below_d)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps
+    loop_step()
+    torch.cuda.synchronize()
+    sparsity = {}
+    for T in W.CS4A_TARGETS:
+        nqb, nkb = vs.geom_counts(w.sides, w.tile, T)[:2]
+        mapped, window, joined, _ = bufs[T]
+        sparsity[str(w.sides[T])] = {
+            "cs4a": 1.0 - float(mapped[0].sum()) / (w.B * w.H * nqb * nkb),
+            "csla_window": 1.0 - float(window[0].sum()) / (nqb * nkb),
+            "union": 1.0 - float(joined[0].sum()) / (w.B * w.H * nqb * nkb)}
+    return {"workload": "cs4a_2b all 13 query scales", "B": w.B, "H": w.H, "decision_side": w.sides[D],
+            "windows": list(windows), "join": "union", "top_p": W.CS4A_TOP_P,
+            "ms_per_step": res["loop"], "dense_ms_per_step": res["dense"],
+            "speedup_vs_dense": res["dense"] / res["loop"],
+            "dense_below_decision_ms": res["below_d"],
+            "count_sparsity": sparsity,
+            "timed": "dense attention at sides 1..24; at 32 dense + score/select + block-sparse over its selection; "
+                     "at 40/48/64 map + CSLA window mask + union + block-sparse + O_cache; dense: all 13 scales"}
 
 
 def cpu_baseline(w, q_np, k_np, v_np, cnt_h, idx_h, sizes, round_bf16, seconds):

@@ -19,8 +19,10 @@ from ._lib import (  # noqa: F401
     build_mask,
     dense_attn_fwd,
     geom_counts,
+    join_lists,
     lib,
     make_geom,
     map_indices,
     ocache_correct,
+    window_radius,
 )

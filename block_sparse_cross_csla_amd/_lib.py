@@ -19,6 +19,7 @@ OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 
 EXPORTS = (
     "varsparse_geom_counts",
+    "varsparse_window_radius",
     "varsparse_build_mask",
     "varsparse_map_indices",
     "varsparse_map_indices_topk",
@@ -26,6 +27,7 @@ EXPORTS = (
     "varsparse_attn_fwd_token",
     "varsparse_dense_attn_fwd",
     "varsparse_ocache_correct",
+    "varsparse_join_lists",
     "varsparse_strerror",
     "varsparse_last_hip_error",
 )
@@ -52,6 +54,7 @@ def _load():
     PI32, PI64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     PG = ctypes.POINTER(Geom)
     lib.varsparse_geom_counts.argtypes = [PG, I32, PI32, PI32, PI64, PI64]
+    lib.varsparse_window_radius.argtypes = [I32, I32, PI32, I32, PI32]
     lib.varsparse_build_mask.argtypes = [PG, I32, I32, PI32, I32, P, P, P, P]
     lib.varsparse_map_indices.argtypes = [PG, I32, I32, I32, F32, I32, I32, I32, I32,
                                           P, PI64, P, PI64, F32, P, P, P, P, P, P]
@@ -60,10 +63,11 @@ def _load():
     lib.varsparse_attn_fwd_token.argtypes = [PG, I32, I32, PI32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32, P]
     lib.varsparse_dense_attn_fwd.argtypes = [I32, I32, I32, I32, I64, I64, P, P, P, P, P, PI64, F32, P]
     lib.varsparse_ocache_correct.argtypes = [I32, I32, I32, I32, I32, P, P, P, PI64, P]
+    lib.varsparse_join_lists.argtypes = [I32, I32, I32, I32, P, P, I32, P, P, I32, P, P, P]
     lib.varsparse_strerror.argtypes = [ctypes.c_int]
     lib.varsparse_strerror.restype = ctypes.c_char_p
     lib.varsparse_last_hip_error.argtypes = []
-    for name in EXPORTS[:8]:
+    for name in EXPORTS[:10]:
         getattr(lib, name).restype = ctypes.c_int
     lib.varsparse_last_hip_error.restype = ctypes.c_int
     return lib
@@ -125,6 +129,15 @@ def geom_counts(sides, tile: int, q_scale: int):
     _check(_LIB.varsparse_geom_counts(ctypes.byref(g), q_scale, ctypes.byref(nqb), ctypes.byref(nkb),
                                       ctypes.byref(nq), ctypes.byref(nk)), "varsparse_geom_counts")
     return nqb.value, nkb.value, nq.value, nk.value
+
+
+def window_radius(n_scales: int, q_scale: int, windows=(3, 5, 7)):
+    """Per-key-scale radii of a query scale under the window schedule of the
+    last len(windows) scales (host only)."""
+    w = (ctypes.c_int32 * len(windows))(*[int(x) for x in windows])
+    out = (ctypes.c_int32 * (q_scale + 1))()
+    _check(_LIB.varsparse_window_radius(n_scales, q_scale, w, len(windows), out), "varsparse_window_radius")
+    return list(out)
 
 
 def build_mask(sides, tile: int, q_scale: int, n_sink: int, radius=None, budget: int = -1,
@@ -259,3 +272,37 @@ def ocache_correct(o_full_d, o_sparse_d, o_t, side_d: int, side_t: int, stream=N
     _check(_LIB.varsparse_ocache_correct(B, H, d, side_d, side_t, _ptr(o_full_d), _ptr(o_sparse_d), _ptr(o_t), st,
                                          _stream(stream)), "varsparse_ocache_correct")
     return o_t
+
+
+JOIN = {"union": 0, "intersection": 1}
+
+
+def join_lists(a_cnt, a_idx, b_cnt, b_idx, join: str = "union", out=None, stream=None):
+    """Per-row union or intersection of two ascending kept-tile lists.
+
+    Lists are int32 cnt [..., rows] / idx [..., rows, nkb] on the device; a
+    list set without leading dimensions is shared by every set of the other.
+    Returns (cnt, idx) with the leading shape of the per-set input."""
+    for x in (a_cnt, a_idx, b_cnt, b_idx):
+        if x.dtype != torch.int32 or not x.is_contiguous():
+            raise ValueError("lists are contiguous int32 tensors")
+    rows, nkb = a_idx.shape[-2], a_idx.shape[-1]
+    if b_idx.shape[-2:] != (rows, nkb) or a_cnt.shape[-1] != rows or b_cnt.shape[-1] != rows:
+        raise ValueError("list shapes differ")
+    if a_cnt.shape[:-1] != a_idx.shape[:-2] or b_cnt.shape[:-1] != b_idx.shape[:-2]:
+        raise ValueError("cnt and idx leading shapes differ")
+    lead_a, lead_b = tuple(a_cnt.shape[:-1]), tuple(b_cnt.shape[:-1])
+    if lead_a and lead_b and lead_a != lead_b:
+        raise ValueError("per-set lists of both sides must have the same leading shape")
+    lead = lead_a or lead_b
+    sets = math.prod(lead) if lead else 1
+    if out is None:
+        out = (torch.empty(*lead, rows, dtype=torch.int32, device=a_cnt.device),
+               torch.empty(*lead, rows, nkb, dtype=torch.int32, device=a_cnt.device))
+    oc, oi = out
+    if tuple(oc.shape) != (*lead, rows) or tuple(oi.shape) != (*lead, rows, nkb):
+        raise ValueError("output shape")
+    _check(_LIB.varsparse_join_lists(sets, rows, nkb, JOIN[join], _ptr(a_cnt), _ptr(a_idx), int(bool(lead_a)),
+                                     _ptr(b_cnt), _ptr(b_idx), int(bool(lead_b)), _ptr(oc), _ptr(oi),
+                                     _stream(stream)), "varsparse_join_lists")
+    return oc, oi

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvarsparse.so")
-SOURCES = ["api.hip", "attn_bf16.hip", "attn_fp32.hip", "csla_mask.hip", "cs4a.hip", "ocache.hip"]
+SOURCES = ["api.hip", "attn_bf16.hip", "attn_fp32.hip", "csla_mask.hip", "cs4a.hip", "ocache.hip", "lists.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -67,6 +67,19 @@ int varsparse_geom_counts(const varsparse_geom* geom, int32_t q_scale, int32_t* 
     return VARSPARSE_OK;
 }
 
+int varsparse_window_radius(int32_t n_scales, int32_t q_scale, const int32_t* windows, int32_t n_windows,
+                            int32_t* radius) {
+    if (n_scales < 1 || n_scales > VARSPARSE_MAX_SCALES || windows == nullptr || radius == nullptr)
+        return VARSPARSE_EINVAL;
+    if (n_windows < 1 || n_windows > n_scales) return VARSPARSE_EINVAL;
+    const int first = n_scales - n_windows;
+    if (q_scale < first || q_scale >= n_scales) return VARSPARSE_EINVAL;
+    const int w = windows[q_scale - first];
+    if (w < 1 || w % 2 == 0) return VARSPARSE_EINVAL;
+    for (int s = 0; s <= q_scale; ++s) radius[s] = (w - 1) / 2;
+    return VARSPARSE_OK;
+}
+
 int varsparse_build_mask(const varsparse_geom* geom, int32_t q_scale, int32_t n_sink, const int32_t* radius,
                          int32_t budget, uint8_t* mask, int32_t* kv_cnt, int32_t* kv_idx, void* stream) {
     int rc = check_geom(geom);
@@ -326,6 +339,23 @@ int varsparse_ocache_correct(int32_t B, int32_t H, int32_t head_dim, int32_t sid
     a.so_b = strides[6]; a.so_h = strides[7]; a.so_t = strides[8];
     a.B = B; a.H = H; a.head_dim = head_dim; a.side_d = side_d; a.side_t = side_t;
     return hip_status(vs::launch_ocache_correct(a, (hipStream_t)stream));
+}
+
+int varsparse_join_lists(int32_t sets, int32_t rows, int32_t nkb, int32_t join,
+                         const int32_t* a_cnt, const int32_t* a_idx, int32_t a_per_set,
+                         const int32_t* b_cnt, const int32_t* b_idx, int32_t b_per_set,
+                         int32_t* out_cnt, int32_t* out_idx, void* stream) {
+    if (sets < 1 || rows < 1 || nkb < 1 || nkb > 65536) return VARSPARSE_EINVAL;
+    if (join != VARSPARSE_JOIN_UNION && join != VARSPARSE_JOIN_INTERSECTION) return VARSPARSE_EINVAL;
+    if ((int64_t)sets * rows >= ((int64_t)1 << 31)) return VARSPARSE_EINVAL;
+    if (!a_cnt || !a_idx || !b_cnt || !b_idx || !out_cnt || !out_idx) return VARSPARSE_EINVAL;
+    if (out_cnt == a_cnt || out_cnt == b_cnt || out_idx == a_idx || out_idx == b_idx) return VARSPARSE_EINVAL;
+    vs::JoinArgs g{};
+    g.a_cnt = a_cnt; g.a_idx = a_idx; g.b_cnt = b_cnt; g.b_idx = b_idx;
+    g.out_cnt = out_cnt; g.out_idx = out_idx;
+    g.sets = sets; g.rows = rows; g.nkb = nkb; g.words = (nkb + 31) / 32; g.join = join;
+    g.a_per_set = a_per_set != 0; g.b_per_set = b_per_set != 0;
+    return hip_status(vs::launch_join_lists(g, (hipStream_t)stream));
 }
 
 const char* varsparse_strerror(int code) {

@@ -87,7 +87,18 @@ struct OcacheArgs {
     int32_t B, H, head_dim, side_d, side_t;
 };
 
+struct JoinArgs {
+    const int32_t* a_cnt;      // [sets or 1][rows]
+    const int32_t* a_idx;      // [sets or 1][rows][nkb]
+    const int32_t* b_cnt;
+    const int32_t* b_idx;
+    int32_t* out_cnt;          // [sets][rows]
+    int32_t* out_idx;          // [sets][rows][nkb]
+    int32_t sets, rows, nkb, words, join, a_per_set, b_per_set;
+};
+
 hipError_t launch_ocache_correct(const OcacheArgs& a, hipStream_t stream);
+hipError_t launch_join_lists(const JoinArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStream_t stream);
 hipError_t launch_attn_fp32(const AttnF32Args& a, int head_dim, bool dense, hipStream_t stream);
 hipError_t launch_csla_mask(const MaskArgs& a, int nqb, hipStream_t stream);

@@ -85,6 +85,18 @@ int varsparse_geom_counts(const varsparse_geom* geom, int32_t q_scale,
                           int32_t* nqb, int32_t* nkb, int64_t* nq, int64_t* nk);
 
 /*
+ * CSLA window schedule (host only, no HIP call; SparVAR, ai.info summary,
+ * "Main Findings", sink ablation item: window sizes [3, 5, 7] for the last 3
+ * scales).  The last n_windows of n_scales query scales use windows[i] (odd,
+ * >= 1, in tokens of each key scale) for query scale n_scales - n_windows + i:
+ * radius[s] = (windows[i] - 1) / 2 for every key scale s = 0..q_scale.
+ * radius: host array of q_scale + 1 entries, written.  EINVAL if q_scale is
+ * not one of the last n_windows scales or a window is even or < 1.
+ */
+int varsparse_window_radius(int32_t n_scales, int32_t q_scale, const int32_t* windows, int32_t n_windows,
+                            int32_t* radius);
+
+/*
  * CSLA block mask of query scale q_scale, compacted to kept-tile lists
  * (SparVAR, ai.info summary, "Methodology in Plain English", second module;
  * "Main Findings", sink ablation).
@@ -246,6 +258,32 @@ int varsparse_ocache_correct(int32_t B, int32_t H, int32_t head_dim, int32_t sid
                              const int64_t strides[9], void* stream);
 
 /* Static description of a status code. */
+/* How varsparse_join_lists combines two kept-tile sets. */
+enum {
+    VARSPARSE_JOIN_UNION = 0,
+    VARSPARSE_JOIN_INTERSECTION = 1
+};
+
+/*
+ * Join of two kept-tile lists per query tile (SparVAR, ai.info summary,
+ * "Main Findings": CS4A, its O_cache correction and CSLA are used together,
+ * CSLA with windows 3/5/7 on the last three scales; "Methodology in Plain
+ * English": CSLA builds its mask without the decision scale).  Used to join a
+ * query scale's CS4A-mapped lists (per (b, h)) with its CSLA lists (shared by
+ * every head).  out row = a row ∪ b row (join 0) or a row ∩ b row (join 1),
+ * ascending, -1 padded to nkb entries; integer only, bit-exact.
+ * Lists (dev int32): cnt [sets][rows], idx [sets][rows][nkb], ascending ids
+ * without repeats; a_per_set / b_per_set = 0 means one list set [rows] shared
+ * by every set.  Entries outside [0, nkb) are ignored and counts are clamped
+ * to [0, nkb].  out_cnt [sets][rows], out_idx [sets][rows][nkb] must not
+ * overlap the inputs.  1 <= nkb <= 65536, sets * rows < 2^31; EINVAL
+ * otherwise, nothing enqueued.
+ */
+int varsparse_join_lists(int32_t sets, int32_t rows, int32_t nkb, int32_t join,
+                         const int32_t* a_cnt, const int32_t* a_idx, int32_t a_per_set,
+                         const int32_t* b_cnt, const int32_t* b_idx, int32_t b_per_set,
+                         int32_t* out_cnt, int32_t* out_idx, void* stream);
+
 const char* varsparse_strerror(int code);
 
 /* The hipError_t of the calling thread's last VARSPARSE_EHIP (0 if none). */

@@ -150,3 +150,36 @@ def test_ocache_validation():
     assert call(o=ctypes.c_void_p((1 << 20) + 8)) == _lib.EINVAL   # misaligned
     bad = (ctypes.c_int64 * 9)(*([128 * 1024, 1024 * 128, 130] * 3))
     assert call(strides=bad) == _lib.EINVAL          # token stride not a multiple of 8
+
+
+def test_join_validation():
+    lib = _lib.lib()
+    p, q, o1, o2 = (ctypes.c_void_p((1 << 20) + 4096 * i) for i in range(4))
+
+    def call(sets=2, rows=64, nkb=172, join=0, ac=p, ai=q, bc=p, bi=q, oc=o1, oi=o2):
+        return lib.varsparse_join_lists(sets, rows, nkb, join, ac, ai, 1, bc, bi, 0, oc, oi, None)
+
+    assert call(sets=0) == _lib.EINVAL
+    assert call(rows=0) == _lib.EINVAL
+    assert call(nkb=0) == _lib.EINVAL
+    assert call(nkb=65537) == _lib.EINVAL
+    assert call(join=2) == _lib.EINVAL
+    assert call(sets=1 << 16, rows=1 << 15) == _lib.EINVAL      # 2^31 rows
+    assert call(ai=None) == _lib.EINVAL
+    assert call(oc=None) == _lib.EINVAL
+    assert call(oi=q) == _lib.EINVAL                             # output aliases an input
+
+
+def test_window_radius_matches_oracle():
+    from oracle import schedule as S
+    for n, windows in ((13, (3, 5, 7)), (16, (3, 5, 7)), (16, (9,)), (5, (1, 3))):
+        for q in range(n - len(windows), n):
+            assert vs.window_radius(n, q, windows) == S.window_radius(n, q, windows)
+    lib = _lib.lib()
+    w = (ctypes.c_int32 * 3)(3, 5, 7)
+    out = (ctypes.c_int32 * 16)()
+    for args in ((13, 9, w, 3), (13, 12, w, 0), (13, 12, w, 14), (0, 0, w, 1), (33, 32, w, 3), (13, 12, None, 3)):
+        assert lib.varsparse_window_radius(*args, out) == _lib.EINVAL
+    even = (ctypes.c_int32 * 3)(3, 4, 7)
+    assert lib.varsparse_window_radius(13, 11, even, 3, out) == _lib.EINVAL
+    assert lib.varsparse_window_radius(13, 11, w, 3, None) == _lib.EINVAL
