@@ -8,9 +8,10 @@
 // Single pass: per key tile, partial sums of exp2(s*c - m) relative to the
 // query's running max m (raised lazily, the partials rescaled when it is);
 // the row total is the sum of the partials.  The key tiles are split between
-// two wave pairs (even / odd tiles) whose maxima and sums are merged exactly
-// at the end.  The QK^T work is the bf16 MFMA tile engine of the attention
-// kernel.  Reductions run in a fixed order: scores are bit-reproducible.
+// four wave pairs (tiles equal mod 4) whose maxima and sums are merged
+// exactly at the end.  QK^T runs on bf16 MFMA (32x32x16) with K staged in
+// LDS ahead of use.  Reductions run in a fixed order: scores are
+// bit-reproducible.
 //
 // cs4a_select_map_kernel: one wave per (batch, head, target query tile).
 // Top-p (or Top-K) on integer-quantised scores (exact, associative) of the
@@ -21,72 +22,57 @@
 
 namespace vs {
 
-// Walk over the key tiles of one parity (tiles par, par + 2, ...), each in
-// halves of up to 4 rows.
-struct TileWalk {
-    int j, half;
+constexpr int kScoreParts = 4;                          // key-tile parts
+constexpr int kScoreStages = 2;                         // LDS ring depth per part
+constexpr int kScoreThreads = 2 * 64 * kScoreParts;     // two query halves per part
+
+// One chunk of the key walk: up to 4 rows x 8 columns of one key tile.
+struct ScoreChunk {
+    int32_t base;       // token of the first key
+    int32_t stride;     // tokens per row of its scale
+    int32_t tile;       // key-tile id
+    int32_t shape;      // rows | cols << 4
 };
 
-__device__ __forceinline__ bool tile_next(TileWalk& w, const DevGeom& g, int nkb, int& tile, int& base, int& stride,
-                                          int& nrows, int& ncols) {
-    if (w.j >= nkb) return false;
-    const int s = scale_of_tile(g, w.j);
-    const int local = w.j - g.tile_base[s];
-    const int nb = g.nb[s], side = g.side[s];
-    const int ta = local / nb, tb = local - ta * nb;
-    const int rows = min(8, side - 8 * ta), cols = min(8, side - 8 * tb);
-    tile = w.j;
-    base = g.tok_off[s] + (8 * ta + 4 * w.half) * side + 8 * tb;
-    stride = side;
-    nrows = min(4, rows - 4 * w.half);
-    ncols = cols;
-    if (w.half == 0 && rows > 4) {
-        w.half = 1;
-    } else {
-        w.half = 0;
-        w.j += 2;
-    }
-    return true;
-}
-
-// Chunks of the tiles of one parity.
-__device__ __forceinline__ int parity_chunks(const DevGeom& g, int nkb, int par) {
-    int n = 0;
-    for (int j = par; j < nkb; j += 2) {
-        const int s = scale_of_tile(g, j);
-        const int local = j - g.tile_base[s];
-        const int ta = local / g.nb[s];
-        n += (min(8, g.side[s] - 8 * ta) > 4) ? 2 : 1;
-    }
-    return n;
-}
-
-// Four waves per decision query tile: waves (2 par + qh) take query rows
-// 4 qh .. 4 qh + 3 and the key tiles of parity par.  Each lane keeps, per key
-// tile of its parity, the partial sum of exp2(s c - m) over its query's keys
-// relative to its running max m (two lane halves of a query are summed into
-// one LDS slot per chunk); at the end the two parities' maxima and sums are
-// merged exactly, every partial is normalised by its query's total, and each
-// key tile's score is summed over its 64 queries in a fixed order.
+// Eight waves per decision query tile: wave w takes query rows
+// 4 (w & 1) .. 4 (w & 1) + 3 (32 queries) and the key tiles of part w >> 1
+// (tiles part, part + 4, ...).  The chunk table (every key tile split in
+// halves of up to 4 rows) is built once per workgroup in LDS, one thread per
+// key tile and a per-part prefix sum, so the walk costs one LDS broadcast
+// read per chunk.  The two waves of a part share its K chunks, loaded
+// HBM -> LDS with global_load_lds (16 B per lane, whole rows per
+// instruction) into a ring of kScoreStages buffers, kScoreStages - 1 chunks
+// ahead of use, one workgroup barrier per step; two workgroups share a CU.
+// Single pass: each lane keeps, per key tile of its part, the partial sum
+// of exp2(s c - m) over its query's keys relative to its running max m
+// (raised lazily, the partials rescaled when it is); at the end the parts'
+// maxima and sums are merged exactly, every partial is normalised by its
+// query's total, and each key tile's score is summed over its 64 queries in
+// a fixed order (bit-reproducible).
 template <int D>
-__global__ __launch_bounds__(256) void cs4a_score_kernel(const ScoreArgs a) {
+__global__ __launch_bounds__(kScoreThreads) void cs4a_score_kernel(const ScoreArgs a) {
     constexpr int KSTEPS = D / 16;
     constexpr int ROWB = D * 2;
     constexpr int CH = D / 8;
     constexpr int STAGE = 32 * ROWB;
     constexpr int RPL = 1024 / ROWB;
-    constexpr int LOADS = 16 / RPL;
+    constexpr int LOADS = 16 / RPL;                                // load instructions per wave per chunk
+    constexpr int NST = kScoreStages;
     constexpr float kLazy = 8.0f;
     extern __shared__ __attribute__((aligned(1024))) char dyn[];
-    char* kst_base = dyn;                                  // [par][buf][STAGE]
-    float* acc = (float*)(dyn + 4 * STAGE);                // [nkb][128]
-    float* mrow = acc + a.nkb * 128;                       // [128]
-    float* lrow = mrow + 128;                              // [128]
+    char* kst_base = dyn;                                          // [part][stage][STAGE]
+    const int tpp = a.nkb / 2 + 2;                                 // table entries per part (>= 2 ceil(nkb / 4))
+    ScoreChunk* table = (ScoreChunk*)(dyn + kScoreParts * NST * STAGE);   // [part][tpp]
+    int* halves = (int*)(table + kScoreParts * tpp);                         // [nkb]
+    int* nchunks = halves + a.nkb;                                 // [part]
+    float* mrow = (float*)(nchunks + kScoreParts);                 // [part][64]
+    float* lrow = mrow + 64 * kScoreParts;                         // [part][64]
+    float* acc = lrow + 64 * kScoreParts;                                       // [nkb][64 queries]
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int qh = wave & 1, par = wave >> 1;
     const int n = lane & 31, g = lane >> 5;
-    const int slot = (2 * par + qh) * 32 + n;              // one per (parity, query)
+    const int q = qh * 32 + n;                                     // query within the tile
     const int bh = blockIdx.x / a.nqb, qt = blockIdx.x - bh * a.nqb;
     const int b = bh / a.H, h = bh - b * a.H;
     const int nkb = a.nkb;
@@ -100,46 +86,74 @@ __global__ __launch_bounds__(256) void cs4a_score_kernel(const ScoreArgs a) {
     for (int s = 0; s < KSTEPS; ++s) qreg[s] = *(const bf16x8*)(qp + 16 * s + 8 * g);
     const __bf16* kh = a.k + b * a.sk_b + h * a.sk_h;
 
-    for (int i = tid; i < nkb * 128; i += 256) acc[i] = 0.0f;
-    const int nch0 = parity_chunks(a.g, nkb, 0), nch1 = parity_chunks(a.g, nkb, 1);
-    const int nch = par ? nch1 : nch0, nmax = max(nch0, nch1);
+    // chunk table: one thread per key tile
+    int my_tile_rows = 0, my_s = 0, my_ta = 0, my_tb = 0;
+    if (tid < nkb) {
+        my_s = scale_of_tile(a.g, tid);
+        const int local = tid - a.g.tile_base[my_s];
+        my_ta = local / a.g.nb[my_s];
+        my_tb = local - my_ta * a.g.nb[my_s];
+        my_tile_rows = min(8, a.g.side[my_s] - 8 * my_ta);
+        halves[tid] = my_tile_rows > 4 ? 2 : 1;
+    }
+    if (tid < kScoreParts) nchunks[tid] = 0;
+    for (int i = tid; i < nkb * 64; i += kScoreThreads) acc[i] = 0.0f;
     __syncthreads();
+    if (tid < nkb) {
+        const int p = tid % kScoreParts;
+        int off = 0;
+        for (int j = p; j < tid; j += kScoreParts) off += halves[j];
+        const int side = a.g.side[my_s];
+        const int cols = min(8, side - 8 * my_tb);
+        for (int hh = 0; hh < halves[tid]; ++hh) {
+            ScoreChunk c;
+            c.base = a.g.tok_off[my_s] + (8 * my_ta + 4 * hh) * side + 8 * my_tb;
+            c.stride = side;
+            c.tile = tid;
+            c.shape = min(4, my_tile_rows - 4 * hh) | (cols << 4);
+            table[p * tpp + off + hh] = c;
+        }
+        if (tid + kScoreParts >= nkb) nchunks[p] = off + halves[tid];   // last tile of its part
+    }
+    __syncthreads();
+    const int nch = nchunks[par];
+    int nmax = 0;
+#pragma unroll
+    for (int p = 0; p < kScoreParts; ++p) nmax = max(nmax, nchunks[p]);
+    const ScoreChunk* mytab = table + par * tpp;
     wait_vmcnt(0);   // Q is in registers before LDS-DMA traffic starts
 
-    const uint32_t kst0 = lds_addr(kst_base) + (uint32_t)(par * 2 * STAGE);
-    auto load = [&](int base, int stride, int nrows, int ncols, uint32_t kst) {
+    const uint32_t kst0 = lds_addr(kst_base) + (uint32_t)(par * NST * STAGE);
+    auto issue = [&](int ci) {
+        const ScoreChunk c = mytab[ci];
+        const int nrows = c.shape & 15, ncols = c.shape >> 4;
+        const uint32_t kst = kst0 + (uint32_t)((ci % NST) * STAGE);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int row = 16 * qh + i * RPL + lane / CH;
             const int lc = (lane % CH) ^ swz<CH>(row);
             const int r = row >> 3, col = row & 7;
             const bool valid = r < nrows && col < ncols;
-            const int t = valid ? base + r * stride + col : base;
+            const int t = valid ? c.base + r * c.stride + col : c.base;
             lds_dma16(kh + t * a.sk_t + lc * 8,
                       __builtin_amdgcn_readfirstlane(kst + (uint32_t)((16 * qh + i * RPL) * ROWB)));
         }
     };
 
-    const float c = a.scale_log2;
+    const float cl = a.scale_log2;
     float m_run = -INFINITY;
-    TileWalk walk{par, 0};
-    int ct = 0, cb = 0, cs = 0, cr = 0, ccn = 0, nt = 0, nbs = 0, ns = 0, nr = 0, nc = 0;
-    if (nch > 0) {
-        tile_next(walk, a.g, nkb, ct, cb, cs, cr, ccn);
-        load(cb, cs, cr, ccn, kst0);
-    }
-    // one workgroup barrier per step for all four waves; a parity with fewer
-    // chunks runs empty steps
+    for (int k = 0; k < NST - 1 && k < nch; ++k) issue(k);
     for (int ci = 0; ci < nmax; ++ci) {
-        wait_vmcnt(0);
+        const int ahead = min(NST - 2, nch - 1 - ci);             // chunks issued after chunk ci
+        if (ahead >= 2) wait_vmcnt(2 * LOADS);
+        else if (ahead == 1) wait_vmcnt(LOADS);
+        else wait_vmcnt(0);
         wg_barrier();
-        const bool has = ci < nch;
-        if (ci + 1 < nch) {
-            tile_next(walk, a.g, nkb, nt, nbs, ns, nr, nc);
-            load(nbs, ns, nr, nc, kst0 + (uint32_t)(((ci + 1) & 1) * STAGE));
-        }
-        if (has) {
-            const char* kst = kst_base + par * 2 * STAGE + (ci & 1) * STAGE;
+        if (ci + NST - 1 < nch) issue(ci + NST - 1);
+        if (ci < nch) {
+            const ScoreChunk c = mytab[ci];
+            const int cr = c.shape & 15, ccn = c.shape >> 4, ct = c.tile;
+            const char* kst = kst_base + (par * NST + ci % NST) * STAGE;
             f32x16 sacc = (f32x16)0.0f;
 #pragma unroll
             for (int s = 0; s < KSTEPS; ++s) {
@@ -161,50 +175,52 @@ __global__ __launch_bounds__(256) void cs4a_score_kernel(const ScoreArgs a) {
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
                 mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
             }
-            const float cand = mx * c;
+            const float cand = mx * cl;
             const bool need = cand > m_run + kLazy;
             if (__ballot(need)) {
                 if (need) {
                     const float alpha = __builtin_amdgcn_exp2f(m_run - cand);
                     if (g == 0)
-                        for (int kt = par; kt <= ct; kt += 2) acc[kt * 128 + slot] *= alpha;
+                        for (int kt = par; kt <= ct; kt += kScoreParts) acc[kt * 64 + q] *= alpha;
                     m_run = cand;
                 }
             }
             float part = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) part += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c, -m_run));
+            for (int i = 0; i < 16; ++i) part += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], cl, -m_run));
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
             part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);   // both halves of the query's keys
-            if (g == 0) acc[ct * 128 + slot] += part;
+            if (g == 0) acc[ct * 64 + q] += part;
         }
-        ct = nt; cb = nbs; cs = ns; cr = nr; ccn = nc;
     }
 
-    // merge the two parities: common max M, total l, then normalise
+    // merge the parts: common max M, total l, then normalise
     float l_mine = 0.0f;
     if (g == 0)
-        for (int kt = par; kt < nkb; kt += 2) l_mine += acc[kt * 128 + slot];
+        for (int kt = par; kt < nkb; kt += kScoreParts) l_mine += acc[kt * 64 + q];
     if (g == 0) {
-        mrow[slot] = m_run;
-        lrow[slot] = l_mine;
+        mrow[par * 64 + q] = m_run;
+        lrow[par * 64 + q] = l_mine;
     }
     __syncthreads();
     if (g == 0) {
-        const int other = (2 * (1 - par) + qh) * 32 + n;
-        const float m_o = mrow[other];
-        const float M = fmaxf(m_run, m_o);
-        const float w_mine = __builtin_amdgcn_exp2f(m_run - M), w_o = __builtin_amdgcn_exp2f(m_o - M);
-        const float l_q = l_mine * w_mine + lrow[other] * w_o;
-        const float f = w_mine / l_q;
-        for (int kt = par; kt < nkb; kt += 2) acc[kt * 128 + slot] *= f;
+        float M = mrow[q];
+#pragma unroll
+        for (int p = 1; p < kScoreParts; ++p) M = fmaxf(M, mrow[p * 64 + q]);
+        float l_q = 0.0f;
+#pragma unroll
+        for (int p = 0; p < kScoreParts; ++p) {
+            const float mp = mrow[p * 64 + q];
+            if (mp != -INFINITY) l_q += lrow[p * 64 + q] * __builtin_amdgcn_exp2f(mp - M);
+        }
+        const float f = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M) / l_q;
+        for (int kt = par; kt < nkb; kt += kScoreParts) acc[kt * 64 + q] *= f;
     }
     __syncthreads();
     float* out = a.scores + ((int64_t)bh * a.nqb + qt) * nkb;
-    for (int kt = tid; kt < nkb; kt += 256) {
-        const int p = kt & 1;
+    for (int kt = tid; kt < nkb; kt += kScoreThreads) {
         float sum = 0.0f;
-        for (int q = 0; q < 64; ++q) sum += acc[kt * 128 + (2 * p + (q >> 5)) * 32 + (q & 31)];
+        for (int qq = 0; qq < 64; ++qq) sum += acc[kt * 64 + qq];
         out[kt] = sum * (1.0f / 64.0f);
     }
 }
@@ -326,9 +342,10 @@ __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a
 }
 
 hipError_t launch_cs4a_score(const ScoreArgs& a, int head_dim, hipStream_t stream) {
-    const int stage = 32 * head_dim * 2;
-    const size_t shmem = 4 * (size_t)stage + (size_t)a.nkb * 128 * sizeof(float) + 256 * sizeof(float);
-    dim3 grid((unsigned)(a.nqb * a.B * a.H)), block(256);
+    const size_t shmem = (size_t)kScoreParts * kScoreStages * 32 * head_dim * 2 +
+                         kScoreParts * (size_t)(a.nkb / 2 + 2) * sizeof(ScoreChunk) + (size_t)(a.nkb + kScoreParts) * sizeof(int) +
+                         2 * 64 * kScoreParts * sizeof(float) + (size_t)a.nkb * 64 * sizeof(float);
+    dim3 grid((unsigned)(a.nqb * a.B * a.H)), block(kScoreThreads);
     if (head_dim == 128) {
         hipError_t e = hipFuncSetAttribute((const void*)cs4a_score_kernel<128>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
