@@ -261,6 +261,7 @@ int varsparse_attn_fwd_token(const varsparse_geom* geom, int32_t q_scale, int32_
     if (q_scale < 0 || q_scale >= geom->n_scales) return VARSPARSE_EINVAL;
     if (geom->side[q_scale] % geom->tile != 0) return VARSPARSE_EINVAL;
     if (n_sink < 0 || n_sink > q_scale || radius == nullptr) return VARSPARSE_EINVAL;
+    if (geom->side[q_scale] > 4096) return VARSPARSE_EUNSUPPORTED;   // projections use 24-bit exact quotients
     if (B < 1 || H < 1) return VARSPARSE_EINVAL;
     if (!q || !k || !v || !o || !strides) return VARSPARSE_EINVAL;
     if ((kv_cnt == nullptr) != (kv_idx == nullptr)) return VARSPARSE_EINVAL;

@@ -313,27 +313,61 @@ __device__ __forceinline__ int div_floor(int num, int den) {
     return q;
 }
 
+// Token mode: per-wave constants of the CSLA rule and the projection of this
+// lane's query onto the scale of the chunks being walked.  Lane s holds the
+// side, token offset and radius of scale s; chunks arrive in ascending
+// order, so the projection is recomputed only when the scale changes (the
+// chunk's row stride is its scale's side, and sides are strictly
+// ascending, so the stride names the scale).
+struct TokenState {
+    int32_t sink_end;              // first token after the sink scales
+    int32_t lside, ltok, lrad;     // this lane's scale (lanes >= n_scales: side 0)
+    int32_t side, off, r, py, px;  // the current chunk scale (side 0: none yet)
+};
+
+__device__ __forceinline__ void token_init(TokenState& ts, const AttnArgs& a, int lane) {
+    ts.lside = ts.ltok = ts.lrad = 0;
+    for (int s = 0; s < a.g.n_scales; ++s) {
+        if (lane == s) {
+            ts.lside = a.g.side[s];
+            ts.ltok = a.g.tok_off[s];
+            ts.lrad = a.radius[s];
+        }
+    }
+    ts.sink_end = __builtin_amdgcn_readlane(ts.ltok, a.n_sink < a.g.n_scales ? a.n_sink : 0);
+    if (a.n_sink >= a.g.n_scales) ts.sink_end = a.g.tok_off[a.g.n_scales];
+    ts.side = 0;
+    ts.off = ts.r = ts.py = ts.px = 0;
+}
+
 // Token-level CSLA keep bits of a tile-half chunk for this lane (value i at
 // key row i/4, column 4g + i%4 of the chunk): a key of scale s at (y', x') is
 // kept iff s is a sink scale, or radius[s] >= 0 and |y' - floor(qy h_s / H)|
 // and |x' - floor(qx h_s / H)| are both <= radius[s] (SparVAR, ai.info
 // summary, "Methodology in Plain English", second module).  Chunks of sink
 // scales keep every key.
-__device__ __forceinline__ uint32_t csla_token_bits(const AttnArgs& a, int32_t base, int qy, int qx, int g) {
-    if (base < a.g.tok_off[a.n_sink]) return 0xffffu;
-    int s = a.n_sink;
-    while (s + 1 < a.g.n_scales && a.g.tok_off[s + 1] <= base) ++s;
-    const int r = a.radius[s];
+__device__ __forceinline__ uint32_t csla_token_bits(TokenState& ts, const Chunk& c, int qy, int qx, int q_side,
+                                                    int g) {
+    if (c.base < ts.sink_end) return 0xffffu;
+    if (c.stride != ts.side) {
+        const uint64_t m = __ballot(ts.lside == c.stride);
+        const int s = m ? __builtin_ctzll(m) : 0;
+        ts.side = c.stride;
+        ts.off = __builtin_amdgcn_readlane(ts.ltok, s);
+        ts.r = m ? __builtin_amdgcn_readlane(ts.lrad, s) : -1;
+        ts.py = div_floor(qy * ts.side, q_side);
+        ts.px = div_floor(qx * ts.side, q_side);
+    }
+    const int r = ts.r;
     if (r < 0) return 0u;
-    const int side = a.g.side[s], local = base - a.g.tok_off[s];
-    const int y0 = __builtin_amdgcn_readfirstlane(div_floor(local, side));
-    const int x0 = local - y0 * side;
-    const int py = div_floor(qy * side, a.q_side), px = div_floor(qx * side, a.q_side);
+    const int local = c.base - ts.off;
+    const int y0 = __builtin_amdgcn_readfirstlane(div_floor(local, ts.side));
+    const int x0 = local - y0 * ts.side;
     uint32_t rows = 0u, cols = 0u;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        rows |= (uint32_t)(abs(y0 + k - py) <= r) << k;
-        cols |= (uint32_t)(abs(x0 + 4 * g + k - px) <= r) << k;
+        rows |= (uint32_t)(abs(y0 + k - ts.py) <= r) << k;
+        cols |= (uint32_t)(abs(x0 + 4 * g + k - ts.px) <= r) << k;
     }
     uint32_t bits = 0u;
 #pragma unroll
@@ -435,6 +469,8 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     st.l_run = 0.0f;
     LoadPlan<D> plan;
     make_plan<D>(plan, wave, lane, a.sk_t, a.sv_t);
+    TokenState ts;
+    if (TOKEN) token_init(ts, a, lane);
 
     while (nch > 0) {
         // descriptors of chunks [win, win + 64) in registers, lane i = chunk win + i
@@ -472,7 +508,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
                 nxt = desc(ci + 1);
                 load_chunk<D>(plan, kh, vh, krb, vrb, nxt, lds0 + 2 * STAGE, lds0 + 3 * STAGE, wave, lane);
             }
-            attend_chunk<D>(st, sm, sm + STAGE, cur, c, lane, TOKEN ? csla_token_bits(a, cur.base, qy, qx, g) : 0xffffu);
+            attend_chunk<D>(st, sm, sm + STAGE, cur, c, lane, TOKEN ? csla_token_bits(ts, cur, qy, qx, a.q_side, g) : 0xffffu);
             if (ci + 1 >= nch) break;
             cur = nxt;
             wait_vmcnt(0);
@@ -482,7 +518,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
                 load_chunk<D>(plan, kh, vh, krb, vrb, nxt, lds0, lds0 + STAGE, wave, lane);
             }
             attend_chunk<D>(st, sm + 2 * STAGE, sm + 3 * STAGE, cur, c, lane,
-                            TOKEN ? csla_token_bits(a, cur.base, qy, qx, g) : 0xffffu);
+                            TOKEN ? csla_token_bits(ts, cur, qy, qx, a.q_side, g) : 0xffffu);
             cur = nxt;
         }
         if (DENSE) break;

@@ -216,7 +216,9 @@ int varsparse_attn_fwd(const varsparse_geom* geom, int32_t q_scale, varsparse_dt
  * kept token pair lies in a listed tile.  With kv_cnt = kv_idx = NULL every key
  * tile is walked: the token-masked dense baseline.
  * radius: host array of q_scale + 1 entries.  bf16, head_dim in {64, 128},
- * tile == 8; layouts and strides as varsparse_attn_fwd.
+ * tile == 8, query side <= 4096 (VARSPARSE_EUNSUPPORTED above: the
+ * projections are exact integer quotients below 2^24); layouts and strides
+ * as varsparse_attn_fwd.
  */
 int varsparse_attn_fwd_token(const varsparse_geom* geom, int32_t q_scale, int32_t n_sink,
                              const int32_t* radius, int32_t B, int32_t H, int32_t head_dim,

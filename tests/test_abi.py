@@ -183,3 +183,23 @@ def test_window_radius_matches_oracle():
     even = (ctypes.c_int32 * 3)(3, 4, 7)
     assert lib.varsparse_window_radius(13, 11, even, 3, out) == _lib.EINVAL
     assert lib.varsparse_window_radius(13, 11, w, 3, None) == _lib.EINVAL
+
+
+def test_attn_token_validation():
+    lib = _lib.lib()
+    rad = (ctypes.c_int32 * 32)(*([2] * 32))
+
+    def call(**kw):
+        return lib.varsparse_attn_fwd_token(
+            kw.get("g", _g()), kw.get("q", 12), kw.get("sink", 5), kw.get("rad", rad), kw.get("B", 2),
+            kw.get("H", 16), kw.get("d", 128), FAKE, FAKE, FAKE, FAKE, None, _strides(GOOD12),
+            kw.get("scale", 0.088), kw.get("cnt", FAKE), kw.get("idx", FAKE), 0, None)
+    assert call(sink=-1) == _lib.EINVAL
+    assert call(sink=13) == _lib.EINVAL                       # more sinks than attended scales
+    assert call(rad=None) == _lib.EINVAL
+    assert call(cnt=None) == _lib.EINVAL                      # lists: both or neither
+    assert call(idx=None) == _lib.EINVAL
+    assert call(d=96) == _lib.EUNSUPPORTED
+    assert call(g=_g(SCHEDULE_13, 4)) == _lib.EUNSUPPORTED    # 8x8 tiles only
+    big = (1, 2, 4, 8, 4104)                                  # query side above 4096
+    assert call(g=_g(big), q=4, sink=2) == _lib.EUNSUPPORTED
