@@ -235,8 +235,11 @@ __device__ __forceinline__ int64_t quantise(float s) {
 // LDS, one quantised score per entry; ranks and prefix masses by broadcast
 // reads), keeps the selection as a bitset in registers (one ballot per 64
 // tiles), then decides every target key tile and compacts the list with
-// ballots.  The wave whose target tile is the first child of its parent also
-// writes the parent's selection (sel_cnt / sel_idx) when asked to.
+// ballots, one key scale at a time: each decision row block's footprint on
+// the key scale is computed once per wave (exact double quotients), and a
+// key tile is kept iff a selected decision tile's row and column footprints
+// both meet it.  The wave whose target tile is the first child of its parent
+// also writes the parent's selection (sel_cnt / sel_idx) when asked to.
 __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a) {
     __shared__ int64_t mq[4][256];   // quantised scores of each wave's parent tile
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -300,42 +303,63 @@ __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a
         return (word >> (id & 63)) & 1;
     };
 
-    // ---- mapping onto the target scale
+    // ---- mapping onto the target scale, one key scale at a time (uniform
+    // loop, ascending ids).  srows[sa]: bit sb set iff decision tile (sa, sb)
+    // is selected; fp[sa]: the rows [lo, hi] of scale s that decision row
+    // block sa covers (the same numbers serve columns: grids are square).
+    __shared__ uint32_t srows[4][16];
+    __shared__ int2 fp[4][16];
+    const int tbD = a.g.tile_base[D];
+    if (lane < nbD) {
+        uint32_t r = 0;
+        for (int sb = 0; sb < nbD; ++sb) r |= (uint32_t)selected(tbD + lane * nbD + sb) << sb;
+        srows[wave][lane] = r;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // this wave's LDS writes before its reads
     int base = 0;
     int32_t* out = a.kv_idx + ((int64_t)bh * a.nqbT + qt) * a.nkbT;
-    for (int c0 = 0; c0 < a.nkbT; c0 += 64) {
-        const int j = c0 + lane;
-        bool keep = false;
-        if (j < a.nkbT) {
-            const int s = scale_of_tile(a.g, j);
-            if (s < a.n_sink) {
-                keep = true;
-            } else if (s < D) {
-                keep = selected(j);
-            } else {
-                const int hs = a.g.side[s], nbs = a.g.nb[s];
-                const int local = j - a.g.tile_base[s];
-                const int ka = local / nbs, kb = local - ka * nbs;
-                const int klo_y = ka * t, khi_y = min(ka * t + t, hs) - 1;
-                const int klo_x = kb * t, khi_x = min(kb * t + t, hs) - 1;
-                for (int sa = 0; sa < nbD && !keep; ++sa) {
-                    const int ey = min(sa * t + t, hD);
-                    const int lo_y = (int)(((int64_t)sa * t * hs) / hD);
-                    const int hi_y = (int)(((int64_t)ey * hs + hD - 1) / hD) - 1;
-                    if (klo_y > hi_y || lo_y > khi_y) continue;
-                    for (int sb = 0; sb < nbD; ++sb) {
-                        if (!selected(a.g.tile_base[D] + sa * nbD + sb)) continue;
-                        const int ex = min(sb * t + t, hD);
-                        const int lo_x = (int)(((int64_t)sb * t * hs) / hD);
-                        const int hi_x = (int)(((int64_t)ex * hs + hD - 1) / hD) - 1;
-                        if (klo_x <= hi_x && lo_x <= khi_x) { keep = true; break; }
-                    }
+    for (int s = 0; s <= a.t_scale; ++s) {
+        const int tb0 = a.g.tile_base[s], tb1 = a.g.tile_base[s + 1];
+        const int hs = a.g.side[s], nbs = a.g.nb[s];
+        if (s >= D) {
+            if (lane < nbD) {
+                const int ey = min(lane * t + t, hD);
+                const int lo = (int)floor((double)((int64_t)lane * t * hs) / (double)hD);
+                const int hi = (int)ceil((double)((int64_t)ey * hs) / (double)hD) - 1;
+                fp[wave][lane] = make_int2(lo, hi);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
+        // decision row (or column) blocks whose footprint meets key row block k
+        auto cover = [&](int k) -> uint32_t {
+            const int klo = k * t, khi = min(k * t + t, hs) - 1;
+            uint32_t m = 0;
+            for (int sa = 0; sa < nbD; ++sa) {
+                const int2 f = fp[wave][sa];
+                m |= (uint32_t)(klo <= f.y && f.x <= khi) << sa;
+            }
+            return m;
+        };
+        for (int c0 = tb0; c0 < tb1; c0 += 64) {
+            const int j = c0 + lane;
+            bool keep = false;
+            if (j < tb1) {
+                if (s < a.n_sink) {
+                    keep = true;
+                } else if (s < D) {
+                    keep = selected(j);
+                } else {
+                    const int local = j - tb0;
+                    const int ka = local / nbs, kb = local - ka * nbs;
+                    const uint32_t cols = cover(kb);
+                    for (uint32_t rows = cover(ka); rows != 0u && !keep; rows &= rows - 1u)
+                        keep = (srows[wave][__builtin_ctz(rows)] & cols) != 0u;
                 }
             }
+            const uint64_t bal = __ballot(keep);
+            if (keep) out[base + __popcll(bal & ((1ull << lane) - 1))] = j;
+            base += __popcll(bal);
         }
-        const uint64_t bal = __ballot(keep);
-        if (keep) out[base + __popcll(bal & ((1ull << lane) - 1))] = j;
-        base += __popcll(bal);
     }
     for (int j = base + lane; j < a.nkbT; j += 64) out[j] = -1;
     if (lane == 0) a.kv_cnt[(int64_t)bh * a.nqbT + qt] = base;
