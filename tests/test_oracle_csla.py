@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from oracle import csla, geometry as G
-from varsparse_inputs import SCHEDULE_13, SCHEDULE_16, TINY_SIDES
+from varsparse_inputs import SCHEDULE_13, SCHEDULE_16, TINY_SIDES, workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "csla_hand.json")
 
@@ -153,3 +153,26 @@ def test_lists_round_trip():
         assert (idx[r, cnt[r]:] == -1).all()
         back[r, idx[r, : cnt[r]]] = True
     assert (back == m).all()
+
+
+@pytest.mark.parametrize("name,count,flop,kmin,kmean,kmax", [
+    ("tiny_fp32", 0.4239, 0.4575, 11, 13.25, 16),
+    ("last_scale_2b", 0.8250, 0.8431, 16, 30.09, 39),
+    ("high_res_128", 0.9426, 0.9482, 19, 38.58, 48),
+])
+def test_workload_sparsity_figures(name, count, flop, kmin, kmean, kmax):
+    """Block sparsity of the workloads' masks against figures derived
+    independently of this oracle (a separate token-level brute force made
+    when the workloads were specified; the pages print none for these
+    shapes): count and token-weighted sparsity to 1e-4, kept tiles per row."""
+    w = {x.name: x for x in W.ALL}[name]
+    m = csla.block_mask(w.sides, w.q_scale, w.tile, w.n_sink, w.radii)
+    c, f = csla.sparsity(m, w.sides, w.q_scale, w.tile)
+    assert abs(c - count) < 1e-4 and abs(f - flop) < 1e-4
+    k = m.sum(axis=1)
+    assert (k.min(), k.max()) == (kmin, kmax) and abs(k.mean() - kmean) < 0.005
+
+
+def test_side48_radius2_sparsity_figure():
+    m = csla.block_mask(SCHEDULE_13, 11, 8, 5, [2] * 12)
+    assert abs(csla.sparsity(m, SCHEDULE_13, 11, 8)[0] - 0.7467) < 1e-4
