@@ -157,3 +157,25 @@ def test_top_k_selection_and_mapping_bit_exact(cs4a_run, frac):
         assert (sc == cnt).all() and (si == idx).all()
         mc, mi = OC.map_indices(cnt, idx, w.sides, r["D"], T, w.tile, w.n_sink)
         assert (kc == mc).all() and (ki == mi).all()
+
+
+def test_large_decision_scale():
+    """Decision scale side 64 of the 16-scale schedule (172 key tiles: the
+    score kernel's largest per-tile accumulator in these workloads), mapped to
+    side 128: scores within tolerance, selection and map bit-exact on the
+    GPU's own scores."""
+    vs = _vs()
+    w = W.HIGH_RES
+    D, T = 12, 15
+    q_d, k, _ = spatial(w, B=1, H=2, q_side=w.sides[D])
+    scores, sc, si, kc, ki = vs.map_indices(w.sides, w.tile, D, T, w.n_sink, W.CS4A_TOP_P,
+                                           q_d=to_device(q_d), k=to_device(k), want_selection=True)
+    torch.cuda.synchronize()
+    s = scores.cpu().numpy()
+    assert s.shape[-1] == 172
+    ref = OC.block_scores(q_d, k, w.sides, D, w.tile, 1 / math.sqrt(w.d))
+    assert np.abs(s - ref).max() <= SCORE_TOL
+    cnt, idx = OC.top_p_select(s, W.CS4A_TOP_P)
+    assert (sc.cpu().numpy() == cnt).all() and (si.cpu().numpy() == idx).all()
+    mc, mi = OC.map_indices(cnt, idx, w.sides, D, T, w.tile, w.n_sink)
+    assert (kc.cpu().numpy() == mc).all() and (ki.cpu().numpy() == mi).all()

@@ -49,7 +49,7 @@ def _dev(x):
 
 
 @pytest.mark.parametrize("join", ["union", "intersection"])
-@pytest.mark.parametrize("nkb", [1, 31, 64, 172, 672, 5000])
+@pytest.mark.parametrize("nkb", [1, 31, 64, 172, 672, 5000, 65536])
 @pytest.mark.parametrize("shared_b", [False, True])
 def test_join_random_bit_exact(join, nkb, shared_b):
     vs = _vs()
