@@ -14,8 +14,8 @@ Readings taken where the pages leave a step open:
 
 * score[Q, K] = (1/|Q|) sum_{q in Q, k in K} P[q, k], P the softmax of
   Q_D K_{<=D}^T / sqrt(d) over all keys of scales 0..D, so each query tile's
-  row of scores sums to 1 (the pages say "sums"; the constant factor does not
-  change any ranking);
+  row of scores sums to 1 (the pages add the weights up per block; the
+  constant factor does not change any ranking);
 * selection keeps the most massive key tiles up to a cumulative mass top_p
   (the crossing tile included); the alternative Top-K rule (the pages give a
   Top-K ratio of about 0.2 as the stable setting, "Main Findings", decision

@@ -16,7 +16,7 @@ Readings taken where the pages leave a step open:
   scale itself is windowed too (its projection is the identity);
 * sink: the first n_sink scales (0-based s < n_sink) are kept whole;
 * blocks: a (query tile, key tile) pair is kept iff any of its token pairs is
-  kept (the "aggregated into blocks" step).
+  kept (the step that turns the token mask into a block mask).
 
 Budget variant (used to sweep block sparsity at fixed cost): per query tile,
 key tiles are ranked by (not sink, admission radius, -scale, id) and the

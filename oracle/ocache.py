@@ -13,7 +13,7 @@ Readings taken where the pages leave a step open:
   output and its sparse one, R = O_full^D - O_sparse^D, per (b, h, query,
   head dim); the sparse output at D is block-sparse attention over the
   decision tiles' own selection (the CS4A lists mapped from D to D);
-* "upsampled" is nearest-neighbour on the token grid, with the same integer
+* the upsampling is nearest-neighbour on the token grid, with the same integer
   projection used everywhere else: target token (y, x) at side h_T takes the
   residual of token (floor(y h_D / h_T), floor(x h_D / h_T)) at side h_D;
 * the correction adds it: O^T = O_sparse^T + up(R).
