@@ -170,6 +170,7 @@ def test_top_k_count():
     assert OC.top_k_count(47, 0.2) == 10            # ceil(9.4)
     assert OC.top_k_count(160, 0.2) == 32            # float32 product 32.0 exactly
     assert OC.top_k_count(5, 0.0001) == 1            # at least one tile
+    assert OC.top_k_count(5, 0.0) == 1               # even for a zero fraction
     assert OC.top_k_count(5, 1.0) == 5
 
 

@@ -136,3 +136,25 @@ def test_union_contains_both_and_shrinks_with_window():
         mu, mx = S.mask_from_lists(u[q]["cnt"], u[q]["idx"]), S.mask_from_lists(x[q]["cnt"], x[q]["idx"])
         assert (mu >= win).all() and (mx <= win).all() and (mx <= mu).all()
         assert mu.sum() > mx.sum()
+
+
+def test_sink_tiles_in_every_sparse_list():
+    """With a selection too small to reach the sinks on its own (top_p 0.05),
+    every sparse scale of the loop, the decision scale included, still lists
+    every sink tile (the sink region is appended to the mapped selection)."""
+    qs, k, v = _inputs()
+    out = S.scale_loop(qs, k, v, SIDES, T, D, SINK, 0.05, (3, 5), DIM ** -0.5)
+    for q in range(D, len(SIDES)):
+        tiles = G.key_tiles(SIDES, q, T)
+        sinks = {j for j, tl in enumerate(tiles) if tl.scale < SINK}
+        cnt, idx = out[q]["cnt"], out[q]["idx"]
+        for row in range(cnt.shape[-1]):
+            kept = set(idx[0, 0, row, : cnt[0, 0, row]].tolist())
+            assert sinks <= kept
+    # not vacuous: some decision rows select fewer than all sink tiles
+    scores = C.block_scores(qs[D], k, SIDES, D, T, DIM ** -0.5).astype(np.float32)
+    sel_cnt, sel_idx = C.top_p_select(scores, 0.05)
+    tiles_d = G.key_tiles(SIDES, D, T)
+    sinks_d = {j for j, tl in enumerate(tiles_d) if tl.scale < SINK}
+    missing = [not sinks_d <= set(sel_idx[0, 0, r, : sel_cnt[0, 0, r]].tolist()) for r in range(sel_cnt.shape[-1])]
+    assert any(missing)
