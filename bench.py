@@ -188,6 +188,15 @@ def main():
     print(f"[bench] token-wise done: dense {tok_dense_ms:.4f} ms, exact sparse {tok_sparse_ms:.4f} ms",
           file=sys.stderr, flush=True)
 
+    # the block-128 variant: 128-query workgroups over pairs of query tiles,
+    # same tensors and lists
+    # (both kernels timed the same way: back-to-back launches on the stream)
+    ref64_ms = timed(lambda: vs.attn_fwd(q, k, v, w.sides, w.tile, w.q_scale, kv_cnt, kv_idx, softmax_scale=scale,
+                                         out=od, lse=lsed, stream=stream), args.steps)
+    pair_ms = timed(lambda: vs.attn_fwd_pair(q, k, v, w.sides, w.tile, w.q_scale, kv_cnt, kv_idx, softmax_scale=scale,
+                                             out=od, lse=lsed, stream=stream), args.steps)
+    print(f"[bench] paired-tile kernel done: {pair_ms:.4f} ms", file=sys.stderr, flush=True)
+
     result = {
         "metric": "last-scale sparse-attn effective TFLOP/s + speedup vs dense attn, 1 MI355X",
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -215,6 +224,9 @@ def main():
                        "block_sparse_ms": attn_ms, "block_vs_token_masked_dense": tok_dense_ms / attn_ms,
                        "token_exact_vs_token_masked_dense": tok_dense_ms / tok_sparse_ms,
                        "pages_block_vs_token_wise": 15.26},
+        "block128_pair": {"ms": pair_ms, "ms_64_query_kernel": ref64_ms, "flop_per_launch": flops,
+                          "tflops": flops / (pair_ms * 1e-3) / 1e12, "vs_64_query_kernel": ref64_ms / pair_ms,
+                          "what": "128-query workgroups over pairs of 8x8 query tiles, union chunk walk"},
         "roofline": {"bound": "mfma", "achieved": flops / (attn_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                      "traffic": TRAFFIC["bytes"] if kernel_sources_sha256() == TRAFFIC["sources_sha256"] else None,

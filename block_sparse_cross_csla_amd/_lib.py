@@ -25,6 +25,7 @@ EXPORTS = (
     "varsparse_map_indices_topk",
     "varsparse_attn_fwd",
     "varsparse_attn_fwd_token",
+    "varsparse_attn_fwd_pair",
     "varsparse_dense_attn_fwd",
     "varsparse_ocache_correct",
     "varsparse_join_lists",
@@ -61,13 +62,14 @@ def _load():
     lib.varsparse_map_indices_topk.argtypes = lib.varsparse_map_indices.argtypes
     lib.varsparse_attn_fwd.argtypes = [PG, I32, I32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32, P]
     lib.varsparse_attn_fwd_token.argtypes = [PG, I32, I32, PI32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32, P]
+    lib.varsparse_attn_fwd_pair.argtypes = [PG, I32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32, P]
     lib.varsparse_dense_attn_fwd.argtypes = [I32, I32, I32, I32, I64, I64, P, P, P, P, P, PI64, F32, P]
     lib.varsparse_ocache_correct.argtypes = [I32, I32, I32, I32, I32, P, P, P, PI64, P]
     lib.varsparse_join_lists.argtypes = [I32, I32, I32, I32, P, P, I32, P, P, I32, P, P, P]
     lib.varsparse_strerror.argtypes = [ctypes.c_int]
     lib.varsparse_strerror.restype = ctypes.c_char_p
     lib.varsparse_last_hip_error.argtypes = []
-    for name in EXPORTS[:10]:
+    for name in EXPORTS[:11]:
         getattr(lib, name).restype = ctypes.c_int
     lib.varsparse_last_hip_error.restype = ctypes.c_int
     return lib
@@ -220,6 +222,24 @@ def attn_fwd(q, k, v, sides, tile: int, q_scale: int, kv_cnt, kv_idx, softmax_sc
     _check(_LIB.varsparse_attn_fwd(ctypes.byref(g), q_scale, _dtype_code(q), B, H, d, _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(out), _ptr(lse), _strides(q, k, v, out), float(scale), _ptr(kv_cnt),
                                    _ptr(kv_idx), per_head, _stream(stream)), "varsparse_attn_fwd")
+    return out, lse
+
+
+def attn_fwd_pair(q, k, v, sides, tile: int, q_scale: int, kv_cnt, kv_idx, softmax_scale=None,
+                  out=None, lse=None, want_lse=True, stream=None):
+    """Block-sparse attention with 128-query workgroups over pairs of query
+    tiles (bf16); same arguments and results as attn_fwd.  Returns (o, lse)."""
+    B, H, nq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, nq, dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    per_head = 1 if kv_cnt.dim() == 3 else 0
+    g = make_geom(sides, tile)
+    _check(_LIB.varsparse_attn_fwd_pair(ctypes.byref(g), q_scale, B, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                        _ptr(lse), _strides(q, k, v, out), float(scale), _ptr(kv_cnt), _ptr(kv_idx),
+                                        per_head, _stream(stream)), "varsparse_attn_fwd_pair")
     return out, lse
 
 

@@ -555,6 +555,325 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     }
 }
 
+// ---- 128-query workgroups over pairs of query tiles (the block-128 variant)
+//
+// One workgroup = four waves = query tiles 2p and 2p + 1 of one (b, h)
+// (128 queries; waves 0, 1 take tile 2p, waves 2, 3 tile 2p + 1, 32 queries
+// each).  The chunk table walks the union of the two tiles' kept-tile lists
+// (membership bitmaps in LDS), each descriptor carrying which of the two
+// tiles keeps it; every chunk is loaded once for both tiles (each wave fills
+// 8 of its 32 key rows) and a wave attends only to the chunks its tile keeps.
+// A leading run of whole scales kept by both tiles is walked as dense
+// 32-token chunks.  Per query the keys attended are exactly its tile's list;
+// only the chunking of the run may differ from the 64-query kernel.
+constexpr int kPairMaxNkb = kPairMaxNkbHost;    // key tiles covered by the LDS bitmaps
+constexpr int kPairStages = 2;                  // LDS ring depth (K and V per stage)
+
+template <int D>
+struct PairPlan {
+    static constexpr int ROWB = D * 2;          // LDS bytes per key row
+    static constexpr int CH = D / 8;            // 16-byte units per row
+    static constexpr int RPL = 1024 / ROWB;     // rows per wave-wide load
+    static constexpr int LOADS = 8 / RPL;       // loads per wave per tensor (8 rows per wave)
+    int32_t kc[LOADS], vc[LOADS];
+};
+
+template <int D>
+__device__ __forceinline__ int pair_slot(int wave, int lane, int i) {
+    using P = PairPlan<D>;
+    return 8 * wave + i * P::RPL + lane / P::CH;            // key slot 0..31 filled by this lane
+}
+
+template <int D>
+__device__ __forceinline__ void make_pair_plan(PairPlan<D>& p, int wave, int lane, int64_t sk_t, int64_t sv_t) {
+    using P = PairPlan<D>;
+#pragma unroll
+    for (int i = 0; i < P::LOADS; ++i) {
+        const int row = pair_slot<D>(wave, lane, i);
+        const int unit = (lane % P::CH) ^ swz<P::CH>(row);
+        p.kc[i] = (row & 7) * (int32_t)(sk_t * 2) + unit * 16;
+        p.vc[i] = (row & 7) * (int32_t)(sv_t * 2) + unit * 16;
+        asm volatile("" : "+v"(p.kc[i]), "+v"(p.vc[i]));
+    }
+}
+
+// Wave `wave` fills key rows [8 wave, 8 wave + 8) of a stage: chunk row `wave`.
+template <int D>
+__device__ __forceinline__ void load_chunk_pair(const PairPlan<D>& p, const __bf16* kh, const __bf16* vh,
+                                                int32_t krb, int32_t vrb, const Chunk& c, uint32_t k_lds,
+                                                uint32_t v_lds, int wave, int lane) {
+    using P = PairPlan<D>;
+    if (c.full) {
+        const int32_t t0 = c.base + wave * c.stride;
+#pragma unroll
+        for (int i = 0; i < P::LOADS; ++i) {
+            const uint32_t dst = (uint32_t)((8 * wave + i * P::RPL) * P::ROWB);
+            lds_dma16_off(kh, t0 * krb + p.kc[i], __builtin_amdgcn_readfirstlane(k_lds + dst));
+            lds_dma16_off(vh, t0 * vrb + p.vc[i], __builtin_amdgcn_readfirstlane(v_lds + dst));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < P::LOADS; ++i) {
+            const int slot = pair_slot<D>(wave, lane, i);
+            const int r = slot >> 3, col = slot & 7;
+            const int unit16 = ((lane % P::CH) ^ swz<P::CH>(slot)) * 16;
+            const bool valid = r < c.nrows && col < c.ncols && slot < c.nvalid;
+            const int32_t tok = valid ? c.base + r * c.stride + col : c.base;
+            const uint32_t dst = (uint32_t)((8 * wave + i * P::RPL) * P::ROWB);
+            lds_dma16_off(kh, tok * krb + unit16, __builtin_amdgcn_readfirstlane(k_lds + dst));
+            lds_dma16_off(vh, tok * vrb + unit16, __builtin_amdgcn_readfirstlane(v_lds + dst));
+        }
+    }
+}
+
+// Walk state of a tile pair: the dense run [cnext, cend), then key tiles
+// from `cursor` on, kept by either tile.
+struct PairWalk {
+    int32_t cnext, cend, cursor, nkb;
+};
+
+// Wave 0 fills the chunk table with the next descriptors of the union walk
+// (bits 30, 31 of the second word: kept by the first / second tile) and
+// returns how many it wrote.
+__device__ __forceinline__ int build_table_pair(PairWalk& w, const DevGeom& g, uint2* table, const uint32_t* bm_a,
+                                                const uint32_t* bm_b, int lane) {
+    int n = 0;
+    if (w.cnext < w.cend) {
+        const int nc = min((w.cend - w.cnext + 31) >> 5, kTableCap);
+        for (int k = lane; k < nc; k += 64) {
+            const int base = w.cnext + 32 * k;
+            table[k] = make_uint2((uint32_t)base, pack_info(8, 4, 8, min(32, w.cend - base)) | (3u << 30));
+        }
+        w.cnext = min(w.cend, w.cnext + 32 * nc);
+        n = nc;
+    }
+    while (w.cursor < w.nkb && kTableCap - n >= 128) {
+        const int id = w.cursor + lane;
+        uint32_t own = 0u;
+        if (id < w.nkb) own = ((bm_a[id >> 5] >> (id & 31)) & 1u) | (((bm_b[id >> 5] >> (id & 31)) & 1u) << 1);
+        const bool valid = own != 0u;
+        int tb = 0, side = g.side[0], off = 0, nb = g.nb[0];
+        for (int s = 1; s < g.n_scales; ++s) {
+            if (id >= g.tile_base[s]) {
+                tb = g.tile_base[s];
+                side = g.side[s];
+                off = g.tok_off[s];
+                nb = g.nb[s];
+            }
+        }
+        const int local = valid ? id - tb : 0;
+        int a = (int)(((float)local + 0.5f) / (float)nb);
+        a -= (a * nb > local);
+        a += ((a + 1) * nb <= local);
+        const int b = local - a * nb, t = g.tile;
+        const int rows = min(t, side - a * t), cols = min(t, side - b * t);
+        const int base = off + a * t * side + b * t;
+        const bool two = valid && rows > 4;
+        const uint64_t vb = __ballot(valid), tb2 = __ballot(two);
+        const uint64_t lt = (1ull << lane) - 1;
+        const int pos = n + __popcll(vb & lt) + __popcll(tb2 & lt);
+        if (valid) {
+            table[pos] = make_uint2((uint32_t)base, pack_info(side, min(4, rows), cols, 32) | (own << 30));
+            if (two)
+                table[pos + 1] = make_uint2((uint32_t)(base + 4 * side), pack_info(side, rows - 4, cols, 32) | (own << 30));
+        }
+        n += __popcll(vb) + __popcll(tb2);
+        w.cursor = min(w.nkb, w.cursor + 64);
+    }
+    return n;
+}
+
+// Leading run of a list: how many of its first entries are 0, 1, 2, ...
+__device__ __forceinline__ int leading_run(const int32_t* idx, int cnt, int lane) {
+    int p = 0;
+    for (;;) {
+        const int v = (p + lane < cnt) ? idx[p + lane] : -1;
+        const uint64_t off = __ballot(v != p + lane);
+        if (off) return p + __builtin_ctzll(off);
+        p += 64;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_pair_bf16_kernel(const AttnArgs a) {
+    constexpr int KSTEPS = D / 16;
+    constexpr int MBLK = D / 32;
+    constexpr int STAGE = 32 * D * 2;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * kPairStages * STAGE];   // [stage][K, V]
+    __shared__ uint2 table[kTableCap];
+    __shared__ uint32_t bm[2][kPairMaxNkb / 32];
+    __shared__ int table_n, run_len[2];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int n = lane & 31, g = lane >> 5;
+    const int tile_sel = wave >> 1, hw = wave & 1;           // which tile of the pair, which query half
+
+    const int npair = (a.nqb + 1) >> 1;
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = work / npair, pr = work - bh * npair;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int qt = 2 * pr + tile_sel;
+    const bool tile_ok = qt < a.nqb;                         // the pair of an odd last tile has one tile
+    const int qt_c = tile_ok ? qt : a.nqb - 1;
+
+    const int nbq = a.q_side >> 3;
+    const int ti = qt_c / nbq, tj = qt_c - ti * nbq;
+    const int64_t tok = (int64_t)(8 * ti + 4 * hw + (n >> 3)) * a.q_side + 8 * tj + (n & 7);
+    const __bf16* kh = a.k + b * a.sk_b + h * a.sk_h;
+    const __bf16* vh = a.v + b * a.sv_b + h * a.sv_h;
+    const int32_t krb = (int32_t)(a.sk_t * 2), vrb = (int32_t)(a.sv_t * 2);
+    const float c = a.scale_log2;
+    const uint32_t lds0 = lds_addr(smem);
+    const char* sm = smem;
+
+    // ---- the two lists: membership bitmaps and the common leading run
+    const int64_t row0 = (a.per_head ? (int64_t)bh * a.nqb : 0) + 2 * pr;
+    const int words = (a.nkb + 31) >> 5;
+    for (int i = threadIdx.x; i < 2 * (kPairMaxNkb / 32); i += 256) (&bm[0][0])[i] = 0u;
+    __syncthreads();
+    {
+        // waves 0, 1: list of tile 2p; waves 2, 3: list of tile 2p + 1 (if any)
+        const int which = wave >> 1;
+        const bool has = 2 * pr + which < a.nqb;
+        const int cnt = has ? min(max(a.kv_cnt[row0 + which], 0), a.nkb) : 0;
+        const int32_t* idx = a.kv_idx + (row0 + which) * a.nkb;
+        for (int e = (wave & 1) * 64 + lane; e < cnt; e += 128) {
+            const int id = idx[e];
+            if (id >= 0 && id < a.nkb) atomicOr(&bm[which][id >> 5], 1u << (id & 31));
+        }
+        if ((wave & 1) == 0) {
+            const int p = has ? leading_run(idx, cnt, lane) : 0;
+            if (lane == 0) run_len[which] = p;
+        }
+    }
+    __syncthreads();
+    PairWalk w;
+    {
+        const int p = min(run_len[0], run_len[1]);
+        int s = 0;
+        while (s < a.g.n_scales && a.g.tile_base[s + 1] <= p) ++s;
+        w.cnext = 0;
+        w.cend = a.g.tok_off[s];
+        w.cursor = a.g.tile_base[s];
+        w.nkb = a.nkb;
+        (void)words;
+    }
+    if (wave == 0) {
+        const int nb = build_table_pair(w, a.g, table, bm[0], bm[1], lane);
+        if (lane == 0) table_n = nb;
+    }
+    __syncthreads();
+    int nch = __builtin_amdgcn_readfirstlane(table_n);
+
+    WaveState<D> st;
+    const __bf16* qp = a.q + b * a.sq_b + h * a.sq_h + tok * a.sq_t;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) st.qreg[s] = *(const bf16x8*)(qp + 16 * s + 8 * g);
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] = (f32x16)0.0f;
+    st.m_run = -1e30f;
+    st.l_run = 0.0f;
+    PairPlan<D> plan;
+    make_pair_plan<D>(plan, wave, lane, a.sk_t, a.sv_t);
+    const uint32_t mine = 1u << tile_sel;
+
+    while (nch > 0) {
+        int win = 0;
+        uint32_t d0, d1;
+        {
+            const uint2 t = table[min(lane, kTableCap - 1)];
+            d0 = t.x;
+            d1 = t.y;
+        }
+        auto desc = [&](int ci, uint32_t& own) -> Chunk {
+            if (ci - win >= 64) {
+                win += 64;
+                const uint2 t = table[min(win + lane, kTableCap - 1)];
+                d0 = t.x;
+                d1 = t.y;
+            }
+            const uint32_t info = __builtin_amdgcn_readlane(d1, ci - win);
+            own = info >> 30;
+            return unpack_chunk((int32_t)__builtin_amdgcn_readlane(d0, ci - win), info);
+        };
+        // ring of kPairStages LDS stages, chunks loaded kPairStages - 1 ahead,
+        // one barrier per chunk: after it every wave has its loads of chunk ci
+        // in LDS and has finished chunk ci - 1, whose stage takes chunk
+        // ci + kPairStages - 1
+        constexpr int NST = kPairStages;
+        constexpr int PER_CHUNK = 2 * PairPlan<D>::LOADS;       // this wave's loads per chunk (K and V)
+        Chunk ring[NST];
+        uint32_t own[NST];
+#pragma unroll
+        for (int k2 = 0; k2 < NST - 1; ++k2) {
+            if (k2 < nch) {
+                ring[k2] = desc(k2, own[k2]);
+                load_chunk_pair<D>(plan, kh, vh, krb, vrb, ring[k2], lds0 + (uint32_t)(2 * k2 * STAGE),
+                                   lds0 + (uint32_t)((2 * k2 + 1) * STAGE), wave, lane);
+            }
+        }
+        for (int ci0 = 0; ci0 < nch; ci0 += NST) {
+#pragma unroll
+            for (int u = 0; u < NST; ++u) {           // stage u holds chunk ci0 + u
+                const int ci = ci0 + u;
+                if (ci >= nch) break;
+                const int ahead = min(NST - 2, nch - 1 - ci);      // chunks issued after chunk ci
+                if (ahead >= 2) wait_vmcnt(2 * PER_CHUNK);
+                else if (ahead == 1) wait_vmcnt(PER_CHUNK);
+                else wait_vmcnt(0);
+                wg_barrier();
+                constexpr int dummy = 0;
+                (void)dummy;
+                const int nu = (u + NST - 1) % NST;                  // stage of chunk ci + NST - 1
+                if (ci + NST - 1 < nch) {
+                    ring[nu] = desc(ci + NST - 1, own[nu]);
+                    load_chunk_pair<D>(plan, kh, vh, krb, vrb, ring[nu], lds0 + (uint32_t)(2 * nu * STAGE),
+                                       lds0 + (uint32_t)((2 * nu + 1) * STAGE), wave, lane);
+                }
+                if (own[u] & mine) attend_chunk<D>(st, sm + 2 * u * STAGE, sm + (2 * u + 1) * STAGE, ring[u], c, lane);
+            }
+        }
+        // long walks: rebuild the table with what remains
+        __syncthreads();
+        if (wave == 0) {
+            const int nb = build_table_pair(w, a.g, table, bm[0], bm[1], lane);
+            if (lane == 0) table_n = nb;
+        }
+        __syncthreads();
+        nch = __builtin_amdgcn_readfirstlane(table_n);
+    }
+
+    // ---- epilogue (as the 64-query kernel)
+    const float l_tot = half_swap_sum(st.l_run);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (tile_ok) {
+        __bf16* op = a.o + b * a.so_b + h * a.so_h + tok * a.so_t;
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x4 val;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) val[e] = (__bf16)(st.oacc[mb][4 * kk + e] * inv);
+                *(bf16x4*)(op + 32 * mb + 8 * kk + 4 * g) = val;
+            }
+        }
+        if (a.lse != nullptr && g == 0) {
+            const int64_t nq_tot = (int64_t)a.q_side * a.q_side;
+            a.lse[(int64_t)bh * nq_tot + tok] =
+                l_tot > 0.0f ? (st.m_run + __builtin_log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+        }
+    }
+}
+
+hipError_t launch_attn_pair_bf16(const AttnArgs& a, int head_dim, hipStream_t stream) {
+    const int64_t blocks = (int64_t)((a.nqb + 1) / 2) * a.B * a.H;
+    dim3 grid((unsigned)blocks), block(256);
+    if (head_dim == 128) hipLaunchKernelGGL(attn_pair_bf16_kernel<128>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(attn_pair_bf16_kernel<64>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStream_t stream) {
     const int64_t nqt = dense ? (a.nq + 63) / 64 : a.nqb;
     const int64_t blocks = nqt * a.B * a.H;

@@ -100,6 +100,8 @@ struct JoinArgs {
 hipError_t launch_ocache_correct(const OcacheArgs& a, hipStream_t stream);
 hipError_t launch_join_lists(const JoinArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStream_t stream);
+constexpr int kPairMaxNkbHost = 4096;   // key tiles the paired-tile kernel's LDS bitmaps cover
+hipError_t launch_attn_pair_bf16(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_attn_fp32(const AttnF32Args& a, int head_dim, bool dense, hipStream_t stream);
 hipError_t launch_csla_mask(const MaskArgs& a, int nqb, hipStream_t stream);
 hipError_t launch_cs4a_score(const ScoreArgs& a, int head_dim, hipStream_t stream);

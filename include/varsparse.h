@@ -203,6 +203,21 @@ int varsparse_attn_fwd(const varsparse_geom* geom, int32_t q_scale, varsparse_dt
                        void* stream);
 
 /*
+ * Block-sparse attention with 128-query workgroups (SparVAR, ai.info
+ * summary, "Main Findings": the block-wise kernel measured with blocks of
+ * 128 and of 64 tokens).  Same operation, arguments, layouts and results
+ * (up to rounding order) as varsparse_attn_fwd with dtype VARSPARSE_BF16:
+ * query tiles 2p and 2p + 1 share one workgroup that walks the union of
+ * their kept-tile lists, loads every key chunk once for both and attends
+ * each tile to its own list only.  tile == 8, head_dim in {64, 128}; at
+ * most 4096 key tiles (VARSPARSE_EUNSUPPORTED above).
+ */
+int varsparse_attn_fwd_pair(const varsparse_geom* geom, int32_t q_scale, int32_t B, int32_t H, int32_t head_dim,
+                            const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int64_t strides[12], float softmax_scale, const int32_t* kv_cnt,
+                            const int32_t* kv_idx, int32_t lists_per_head, void* stream);
+
+/*
  * Token-exact CSLA attention (SparVAR, ai.info summary, "Methodology in Plain
  * English", second module: the token-level sink + window mask; "Key
  * Contributions" item 3: the naive token-wise sparse attention baseline).

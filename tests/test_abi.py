@@ -203,3 +203,24 @@ def test_attn_token_validation():
     assert call(g=_g(SCHEDULE_13, 4)) == _lib.EUNSUPPORTED    # 8x8 tiles only
     big = (1, 2, 4, 8, 4104)                                  # query side above 4096
     assert call(g=_g(big), q=4, sink=2) == _lib.EUNSUPPORTED
+
+
+def test_attn_pair_validation():
+    lib = _lib.lib()
+
+    def call(**kw):
+        return lib.varsparse_attn_fwd_pair(
+            kw.get("g", _g()), kw.get("q", 12), kw.get("B", 2), kw.get("H", 16), kw.get("d", 128),
+            kw.get("qp", FAKE), FAKE, FAKE, FAKE, None, _strides(kw.get("st", GOOD12)), kw.get("scale", 0.088),
+            kw.get("cnt", FAKE), FAKE, kw.get("per_head", 0), None)
+    assert call(d=96) == _lib.EUNSUPPORTED
+    assert call(g=_g(SCHEDULE_13, 4)) == _lib.EUNSUPPORTED    # 8x8 tiles only
+    assert call(B=0) == _lib.EINVAL
+    assert call(scale=0.0) == _lib.EINVAL
+    assert call(qp=None) == _lib.EINVAL
+    assert call(cnt=None) == _lib.EINVAL
+    assert call(qp=MISALIGNED) == _lib.EINVAL
+    assert call(per_head=2) == _lib.EINVAL
+    assert call(q=13) == _lib.EINVAL
+    big = (8, 16, 32, 64, 128, 256, 512)                      # 5461 key tiles
+    assert call(g=_g(big), q=6) == _lib.EUNSUPPORTED
