@@ -199,3 +199,24 @@ def test_full_size_high_res_sampled():
     ro, rl = OA.block_sparse_attention(q, k, v, w.sides, w.q_scale, w.tile, mc, mi, 1 / math.sqrt(w.d),
                                        q_tiles=[0, 15, 100, 137, 255], bh=[(0, 0), (0, 9), (0, 15)])
     _compare(o, lse, ro, rl, BF16_TOL, "high-res")
+
+
+@pytest.mark.parametrize("per_head", [True, False])
+def test_bf16_eight_heads_every_tile(per_head):
+    """B H = 8 (one head per XCD range), shared and per-head random lists of
+    mixed densities: every query tile of every head computed and right."""
+    vs = _vs()
+    sides, qs, t = SCHEDULE_13, 10, 8
+    B, H, d = 2, 4, 128
+    nqb, nkb, nq, nk = G.counts(sides, qs, t)
+    rng = np.random.default_rng(77)
+    shape = (B, H, nqb, nkb) if per_head else (nqb, nkb)
+    keep = rng.random(shape) < rng.choice([0.02, 0.2, 0.6], size=shape[:-1] + (1,))
+    cnt, idx = lists(keep)
+    q, k, v = gaussian(8, 81, B, H, nq, nk, d)
+    o, lse = vs.attn_fwd(to_device(q), to_device(k), to_device(v), sides, t, qs,
+                         torch.from_numpy(cnt).cuda(), torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    ro, rl = OA.block_sparse_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                       sides, qs, t, cnt, idx, 1 / math.sqrt(d))
+    _compare(o, lse, ro, rl, BF16_TOL, f"eight heads per_head={per_head}")
