@@ -220,3 +220,30 @@ def test_bf16_eight_heads_every_tile(per_head):
     ro, rl = OA.block_sparse_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
                                        sides, qs, t, cnt, idx, 1 / math.sqrt(d))
     _compare(o, lse, ro, rl, BF16_TOL, f"eight heads per_head={per_head}")
+
+
+@pytest.mark.parametrize("gain", [4.0, 16.0])
+def test_bf16_large_scores_lazy_rescale(gain):
+    """Q and K scaled up (scores of hundreds, softmax rows dominated by a few
+    keys and running maxima raised many times over a row): sparse and dense
+    attention stay within the bf16 bar of the float64 oracle."""
+    vs = _vs()
+    sides, qs, t = SCHEDULE_13, 10, 8
+    B, H, d = 1, 2, 128
+    nqb, nkb, nq, nk = G.counts(sides, qs, t)
+    q, k, v = gaussian(9, 91, B, H, nq, nk, d, bf16=False)
+    from varsparse_inputs import round_bf16
+    q, k, v = round_bf16(q * np.float32(gain)), round_bf16(k * np.float32(gain / 4)), round_bf16(v)
+    cnt, idx, _ = vs.build_mask(sides, t, qs, 5, radius=(2,) * (qs + 1))
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    o, lse = vs.attn_fwd(qd, kd, vd, sides, t, qs, cnt, idx)
+    od, lsed = vs.dense_attn_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    mc, mi = lists(oracle_mask(sides, qs, t, 5, (2,) * (qs + 1)))
+    scale = 1 / math.sqrt(d)
+    ro, rl = OA.block_sparse_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                       sides, qs, t, mc, mi, scale)
+    _compare(o, lse, ro, rl, BF16_TOL, f"large scores sparse gain={gain}")
+    rows = np.arange(0, nq, 37)
+    rdo, rdl = OA.dense_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), scale, q_rows=rows)
+    _compare(od, lsed, rdo, rdl, BF16_TOL, f"large scores dense gain={gain}")
