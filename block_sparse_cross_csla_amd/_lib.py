@@ -123,6 +123,46 @@ def _dtype_code(t):
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def _need(cond, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_qkvo(q, k, v, out, lse, nq_expect: int, nk_min: int, bf16_only: bool):
+    """Host-side checks that keep every kernel access inside the tensors: the
+    library sees only pointers and strides."""
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v are [B, H, tokens, head_dim]")
+    B, H, nq, d = q.shape
+    _need(nq == nq_expect, f"q holds {nq} tokens per head, the query scale has {nq_expect}")
+    for name, t in (("k", k), ("v", v)):
+        _need(t.shape[0] == B and t.shape[1] == H and t.shape[3] == d, f"{name} {tuple(t.shape)} does not match q")
+        _need(t.shape[2] >= nk_min, f"{name} holds {t.shape[2]} tokens, the attended cache needs {nk_min}")
+    _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    _need(len({q.dtype, k.dtype, v.dtype, out.dtype}) == 1, "q, k, v and out must share one dtype")
+    if bf16_only:
+        _need(q.dtype == torch.bfloat16, "this entry point takes bfloat16 tensors")
+    if lse is not None:
+        _need(lse.dtype == torch.float32 and lse.is_contiguous() and lse.numel() == B * H * nq,
+              "lse is a contiguous float32 [B, H, nq] tensor")
+
+
+def _check_lists(kv_cnt, kv_idx, B: int, H: int, nqb: int, nkb: int):
+    _need(kv_cnt.dtype == torch.int32 and kv_idx.dtype == torch.int32, "lists are int32")
+    _need(kv_cnt.is_contiguous() and kv_idx.is_contiguous(), "lists must be contiguous")
+    if kv_cnt.dim() == 1:
+        _need(tuple(kv_cnt.shape) == (nqb,) and tuple(kv_idx.shape) == (nqb, nkb),
+              f"shared lists are kv_cnt [{nqb}] and kv_idx [{nqb}, {nkb}]")
+    else:
+        _need(tuple(kv_cnt.shape) == (B, H, nqb) and tuple(kv_idx.shape) == (B, H, nqb, nkb),
+              f"per-head lists are kv_cnt [{B}, {H}, {nqb}] and kv_idx [{B}, {H}, {nqb}, {nkb}]")
+
+
+def _on_gpu(*tensors):
+    """Last check before a call into the library: every tensor on one GPU."""
+    ts = [t for t in tensors if t is not None]
+    _need(all(t.is_cuda and t.device == ts[0].device for t in ts), "tensors must be on one GPU")
+
+
 def geom_counts(sides, tile: int, q_scale: int):
     """(nqb, nkb, nq, nk) of a query scale (host only)."""
     g = make_geom(sides, tile)
@@ -147,12 +187,19 @@ def build_mask(sides, tile: int, q_scale: int, n_sink: int, radius=None, budget:
     """CSLA kept-tile lists: (kv_cnt int32 [nqb], kv_idx int32 [nqb, nkb], mask uint8 [nqb, nkb] or None).
     ``out`` may pass preallocated (kv_cnt, kv_idx, mask)."""
     nqb, nkb, _, _ = geom_counts(sides, tile, q_scale)
+    _need(radius is None or len(radius) >= q_scale + 1, "radius needs one entry per attended scale")
     if out is None:
         kv_cnt = torch.empty(nqb, dtype=torch.int32, device=device)
         kv_idx = torch.empty(nqb, nkb, dtype=torch.int32, device=device)
         mask = torch.empty(nqb, nkb, dtype=torch.uint8, device=device) if want_mask else None
     else:
         kv_cnt, kv_idx, mask = out
+        _need(tuple(kv_cnt.shape) == (nqb,) and tuple(kv_idx.shape) == (nqb, nkb), "out lists have the wrong shape")
+        _need(kv_cnt.dtype == torch.int32 and kv_idx.dtype == torch.int32 and kv_idx.is_contiguous(),
+              "out lists are contiguous int32")
+        _need(mask is None or (tuple(mask.shape) == (nqb, nkb) and mask.dtype == torch.uint8 and mask.is_contiguous()),
+              "out mask is a contiguous uint8 [nqb, nkb] tensor")
+    _on_gpu(kv_cnt, kv_idx, mask)
     g = make_geom(sides, tile)
     rad = None
     if radius is not None:
@@ -184,6 +231,17 @@ def map_indices(sides, tile: int, d_scale: int, t_scale: int, n_sink: int, top_p
         kv_idx = torch.empty(B, H, nqbT, nkbT, dtype=torch.int32, device=device)
     else:
         kv_cnt, kv_idx = out
+    _need(tuple(scores.shape) == (B, H, nqbD, nkbD) and scores.dtype == torch.float32 and scores.is_contiguous(),
+          f"scores is a contiguous float32 [{B}, {H}, {nqbD}, {nkbD}] tensor")
+    _check_lists(kv_cnt, kv_idx, B, H, nqbT, nkbT)
+    _need(kv_cnt.dim() == 3, "target lists are per (b, h)")
+    if q_d is not None:
+        _need(k is not None and k.dim() == 4 and tuple(k.shape[:2]) == (B, H) and k.shape[3] == d,
+              "k must be [B, H, tokens, head_dim] like q_d")
+        _need(q_d.shape[2] == geom_counts(sides, tile, d_scale)[2], "q_d must hold the decision scale's tokens")
+        _need(k.shape[2] >= geom_counts(sides, tile, d_scale)[3], "k holds fewer tokens than the decision scale attends")
+        _need(q_d.dtype == k.dtype, "q_d and k share one dtype")
+    _on_gpu(q_d, k, scores, kv_cnt, kv_idx)
     sel_cnt = sel_idx = None
     if want_selection:
         sel_cnt = torch.empty(B, H, nqbD, dtype=torch.int32, device=device)
@@ -216,6 +274,10 @@ def attn_fwd(q, k, v, sides, tile: int, q_scale: int, kv_cnt, kv_idx, softmax_sc
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty(B, H, nq, dtype=torch.float32, device=q.device)
+    nqb, nkb, nq_s, nk_s = geom_counts(sides, tile, q_scale)
+    _check_qkvo(q, k, v, out, lse, nq_s, nk_s, bf16_only=False)
+    _check_lists(kv_cnt, kv_idx, B, H, nqb, nkb)
+    _on_gpu(q, k, v, out, lse, kv_cnt, kv_idx)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     per_head = 1 if kv_cnt.dim() == 3 else 0
     g = make_geom(sides, tile)
@@ -234,6 +296,10 @@ def attn_fwd_pair(q, k, v, sides, tile: int, q_scale: int, kv_cnt, kv_idx, softm
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty(B, H, nq, dtype=torch.float32, device=q.device)
+    nqb, nkb, nq_s, nk_s = geom_counts(sides, tile, q_scale)
+    _check_qkvo(q, k, v, out, lse, nq_s, nk_s, bf16_only=True)
+    _check_lists(kv_cnt, kv_idx, B, H, nqb, nkb)
+    _on_gpu(q, k, v, out, lse, kv_cnt, kv_idx)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     per_head = 1 if kv_cnt.dim() == 3 else 0
     g = make_geom(sides, tile)
@@ -253,6 +319,13 @@ def attn_fwd_token(q, k, v, sides, tile: int, q_scale: int, n_sink: int, radius,
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty(B, H, nq, dtype=torch.float32, device=q.device)
+    nqb, nkb, nq_s, nk_s = geom_counts(sides, tile, q_scale)
+    _check_qkvo(q, k, v, out, lse, nq_s, nk_s, bf16_only=True)
+    _need((kv_cnt is None) == (kv_idx is None), "pass both lists or neither")
+    if kv_cnt is not None:
+        _check_lists(kv_cnt, kv_idx, B, H, nqb, nkb)
+    _need(len(radius) >= q_scale + 1, "radius needs one entry per attended scale")
+    _on_gpu(q, k, v, out, lse, kv_cnt, kv_idx)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     per_head = 1 if (kv_cnt is not None and kv_cnt.dim() == 3) else 0
     rad = (ctypes.c_int32 * (q_scale + 1))(*[int(r) for r in radius[: q_scale + 1]])
@@ -271,6 +344,9 @@ def dense_attn_fwd(q, k, v, softmax_scale=None, out=None, lse=None, want_lse=Tru
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty(B, H, nq, dtype=torch.float32, device=q.device)
+    _check_qkvo(q, k, v, out, lse, nq, nk, bf16_only=False)
+    _need(v.shape[2] >= nk, "v holds fewer tokens than k")
+    _on_gpu(q, k, v, out, lse)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     _check(_LIB.varsparse_dense_attn_fwd(_dtype_code(q), B, H, d, nq, nk, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                          _ptr(lse), _strides(q, k, v, out), float(scale), _stream(stream)),
@@ -288,6 +364,8 @@ def ocache_correct(o_full_d, o_sparse_d, o_t, side_d: int, side_t: int, stream=N
         raise ValueError("token counts do not match the sides")
     if any(t.stride(-1) != 1 for t in (o_full_d, o_sparse_d, o_t)):
         raise ValueError("the head dimension must be contiguous")
+    _need(all(t.dtype == torch.bfloat16 for t in (o_full_d, o_sparse_d, o_t)), "O_cache tensors are bfloat16")
+    _on_gpu(o_full_d, o_sparse_d, o_t)
     st = (ctypes.c_int64 * 9)(*o_full_d.stride()[:3], *o_sparse_d.stride()[:3], *o_t.stride()[:3])
     _check(_LIB.varsparse_ocache_correct(B, H, d, side_d, side_t, _ptr(o_full_d), _ptr(o_sparse_d), _ptr(o_t), st,
                                          _stream(stream)), "varsparse_ocache_correct")
