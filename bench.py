@@ -276,10 +276,12 @@ def bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev):
         nks[T] = nk
     scale = 1.0 / math.sqrt(w.d)
 
+    target_lists = [lists[T] for T in W.CS4A_TARGETS]
+
     def step():
-        for i, T in enumerate(W.CS4A_TARGETS):
-            vs.map_indices(w.sides, w.tile, D, T, w.n_sink, W.CS4A_TOP_P, q_d=q_d if i == 0 else None,
-                           k=k, scores=scores, out=lists[T], stream=stream)
+        # scores at the decision scale, then the lists of the three targets in one launch
+        vs.map_indices_multi(w.sides, w.tile, D, W.CS4A_TARGETS, w.n_sink, W.CS4A_TOP_P, q_d=q_d, k=k,
+                             scores=scores, out=target_lists, stream=stream)
         for T in W.CS4A_TARGETS:
             vs.attn_fwd(qs[T], k[:, :, : nks[T]], v[:, :, : nks[T]], w.sides, w.tile, T, *lists[T],
                         softmax_scale=scale, out=outs[T], want_lse=False, stream=stream)
@@ -350,7 +352,8 @@ def bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev):
             "speedup_vs_dense": res["dense"] / res["sparse"],
             "attention_tflop_per_step": flops / 1e12,
             "effective_tflops": flops / (res["sparse"] * 1e-3) / 1e12,
-            "timed": "score + select + map (3 targets) + 3 block-sparse attentions; dense: 3 dense attentions",
+            "timed": "score + one select/map launch for the 3 targets + 3 block-sparse attentions; "
+                     "dense: 3 dense attentions",
             "ocache": {"ms_per_step": res["ocache"],
                        "timed": "map D->D + block-sparse attention at D + 3 corrections",
                        "decision_full_attention_ms": res["full_d"],
@@ -394,16 +397,18 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
         vs.dense_attn_fwd(qs[s], k[:, :, : nks[s]], v[:, :, : nks[s]], softmax_scale=scale, out=outs[s],
                           want_lse=False, stream=stream)
 
+    multi_out = [lists_d] + [bufs[T][0] for T in W.CS4A_TARGETS]
+
     def loop_step():
         for s in range(D + 1):
             dense_at(s)
-        vs.map_indices(w.sides, w.tile, D, D, w.n_sink, W.CS4A_TOP_P, q_d=qs[D], k=k, scores=scores, out=lists_d,
-                       stream=stream)
+        # the decision scale's scores and the lists of itself and every later scale, in one launch
+        vs.map_indices_multi(w.sides, w.tile, D, [D, *W.CS4A_TARGETS], w.n_sink, W.CS4A_TOP_P, q_d=qs[D], k=k,
+                             scores=scores, out=multi_out, stream=stream)
         vs.attn_fwd(qs[D], k[:, :, : nks[D]], v[:, :, : nks[D]], w.sides, w.tile, D, *lists_d, softmax_scale=scale,
                     out=o_sparse_d, want_lse=False, stream=stream)
         for T in W.CS4A_TARGETS:
             mapped, window, joined, radius = bufs[T]
-            vs.map_indices(w.sides, w.tile, D, T, w.n_sink, W.CS4A_TOP_P, scores=scores, out=mapped, stream=stream)
             vs.build_mask(w.sides, w.tile, T, w.n_sink, radius=radius, out=(*window, None), stream=stream)
             vs.join_lists(*mapped, *window, join="union", out=joined, stream=stream)
             vs.attn_fwd(qs[T], k[:, :, : nks[T]], v[:, :, : nks[T]], w.sides, w.tile, T, *joined,
@@ -447,8 +452,9 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
             "speedup_vs_dense": res["dense"] / res["loop"],
             "dense_below_decision_ms": res["below_d"],
             "count_sparsity": sparsity,
-            "timed": "dense attention at sides 1..24; at 32 dense + score/select + block-sparse over its selection; "
-                     "at 40/48/64 map + CSLA window mask + union + block-sparse + O_cache; dense: all 13 scales"}
+            "timed": "dense attention at sides 1..24; at 32 dense + scores + one select/map launch for 32/40/48/64 + "
+                     "block-sparse over its own selection; at 40/48/64 CSLA window mask + union + block-sparse + "
+                     "O_cache; dense: all 13 scales"}
 
 
 def cpu_baseline(w, q_np, k_np, v_np, cnt_h, idx_h, sizes, round_bf16, seconds):

@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     lib,
     make_geom,
     map_indices,
+    map_indices_multi,
     ocache_correct,
     window_radius,
 )

@@ -23,6 +23,7 @@ EXPORTS = (
     "varsparse_build_mask",
     "varsparse_map_indices",
     "varsparse_map_indices_topk",
+    "varsparse_map_indices_multi",
     "varsparse_attn_fwd",
     "varsparse_attn_fwd_token",
     "varsparse_attn_fwd_pair",
@@ -62,6 +63,8 @@ def _load():
     lib.varsparse_map_indices_topk.argtypes = lib.varsparse_map_indices.argtypes
     lib.varsparse_attn_fwd.argtypes = [PG, I32, I32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32, P]
     lib.varsparse_attn_fwd_token.argtypes = [PG, I32, I32, PI32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32, P]
+    lib.varsparse_map_indices_multi.argtypes = [PG, I32, I32, PI32, I32, I32, F32, I32, I32, I32, I32,
+                                                P, PI64, P, PI64, F32, P, P, P, P]
     lib.varsparse_attn_fwd_pair.argtypes = [PG, I32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32, P]
     lib.varsparse_dense_attn_fwd.argtypes = [I32, I32, I32, I32, I64, I64, P, P, P, P, P, PI64, F32, P]
     lib.varsparse_ocache_correct.argtypes = [I32, I32, I32, I32, I32, P, P, P, PI64, P]
@@ -69,7 +72,7 @@ def _load():
     lib.varsparse_strerror.argtypes = [ctypes.c_int]
     lib.varsparse_strerror.restype = ctypes.c_char_p
     lib.varsparse_last_hip_error.argtypes = []
-    for name in EXPORTS[:11]:
+    for name in EXPORTS[:12]:
         getattr(lib, name).restype = ctypes.c_int
     lib.varsparse_last_hip_error.restype = ctypes.c_int
     return lib
@@ -263,6 +266,64 @@ def map_indices(sides, tile: int, d_scale: int, t_scale: int, n_sink: int, top_p
               _ptr(q_d), qs, _ptr(k), ks, float(scale), _ptr(scores),
               _ptr(sel_cnt), _ptr(sel_idx), _ptr(kv_cnt), _ptr(kv_idx), _stream(stream)), name)
     return scores, sel_cnt, sel_idx, kv_cnt, kv_idx
+
+
+SELECT = {"top_p": 0, "top_k": 1}
+
+
+def map_indices_multi(sides, tile: int, d_scale: int, t_scales, n_sink: int, param: float, rule: str = "top_p",
+                      q_d=None, k=None, softmax_scale=None, scores=None, out=None, stream=None):
+    """CS4A onto several target scales in one launch: scores (computed when q_d
+    is given, else taken from ``scores``), then per target the lists
+    map_indices would write.  Returns (scores, [(kv_cnt, kv_idx) per target])."""
+    t_scales = [int(t) for t in t_scales]
+    _need(1 <= len(t_scales) <= 8, "one to eight target scales")
+    if q_d is not None:
+        B, H, _, d = q_d.shape
+        device = q_d.device
+    else:
+        B, H = scores.shape[:2]
+        d = 0
+        device = scores.device
+    nqbD, nkbD, nqD, nkD = geom_counts(sides, tile, d_scale)
+    if scores is None:
+        scores = torch.empty(B, H, nqbD, nkbD, dtype=torch.float32, device=device)
+    _need(tuple(scores.shape) == (B, H, nqbD, nkbD) and scores.dtype == torch.float32 and scores.is_contiguous(),
+          f"scores is a contiguous float32 [{B}, {H}, {nqbD}, {nkbD}] tensor")
+    if out is None:
+        out = []
+        for t in t_scales:
+            nqbT, nkbT, _, _ = geom_counts(sides, tile, t)
+            out.append((torch.empty(B, H, nqbT, dtype=torch.int32, device=device),
+                        torch.empty(B, H, nqbT, nkbT, dtype=torch.int32, device=device)))
+    _need(len(out) == len(t_scales), "one output pair per target scale")
+    for t, (c, i) in zip(t_scales, out):
+        nqbT, nkbT, _, _ = geom_counts(sides, tile, t)
+        _check_lists(c, i, B, H, nqbT, nkbT)
+        _need(c.dim() == 3, "target lists are per (b, h)")
+    g = make_geom(sides, tile)
+    if q_d is not None:
+        _need(k is not None and k.dim() == 4 and tuple(k.shape[:2]) == (B, H) and k.shape[3] == d,
+              "k must be [B, H, tokens, head_dim] like q_d")
+        _need(q_d.shape[2] == nqD, "q_d must hold the decision scale's tokens")
+        _need(k.shape[2] >= nkD, "k holds fewer tokens than the decision scale attends")
+        _need(q_d.dtype == k.dtype, "q_d and k share one dtype")
+        _need(q_d.stride(-1) == 1 and k.stride(-1) == 1, "the head dimension must be contiguous")
+        scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+        qs = (ctypes.c_int64 * 3)(*q_d.stride()[:3])
+        ks = (ctypes.c_int64 * 3)(*k.stride()[:3])
+        dt = _dtype_code(q_d)
+    else:
+        scale, qs, ks, dt = 1.0, None, None, BF16
+    _on_gpu(q_d, k, scores, *[x for pair in out for x in pair])
+    n = len(t_scales)
+    ts = (ctypes.c_int32 * n)(*t_scales)
+    cnts = (ctypes.c_void_p * n)(*[c.data_ptr() for c, _ in out])
+    idxs = (ctypes.c_void_p * n)(*[i.data_ptr() for _, i in out])
+    _check(_LIB.varsparse_map_indices_multi(ctypes.byref(g), d_scale, n, ts, n_sink, SELECT[rule], float(param), dt,
+                                            B, H, d, _ptr(q_d), qs, _ptr(k), ks, float(scale), _ptr(scores), cnts,
+                                            idxs, _stream(stream)), "varsparse_map_indices_multi")
+    return scores, list(out)
 
 
 def attn_fwd(q, k, v, sides, tile: int, q_scale: int, kv_cnt, kv_idx, softmax_scale=None,

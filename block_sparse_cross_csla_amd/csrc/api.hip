@@ -112,28 +112,49 @@ int varsparse_build_mask(const varsparse_geom* geom, int32_t q_scale, int32_t n_
 namespace {
 
 // CS4A with selection rule 0 (top-p, param = p) or 1 (Top-K fraction).
-int map_indices_impl(const varsparse_geom* geom, int32_t d_scale, int32_t t_scale, int32_t n_sink, int rule,
-                     float top_p, varsparse_dtype dtype, int32_t B, int32_t H, int32_t head_dim,
-                     const void* q_d, const int64_t q_strides[3], const void* k,
+int map_indices_impl(const varsparse_geom* geom, int32_t d_scale, int32_t n_targets, const int32_t* t_scales,
+                     int32_t n_sink, int rule, float top_p, varsparse_dtype dtype, int32_t B, int32_t H,
+                     int32_t head_dim, const void* q_d, const int64_t q_strides[3], const void* k,
                      const int64_t k_strides[3], float softmax_scale, float* scores,
-                     int32_t* sel_cnt, int32_t* sel_idx, int32_t* kv_cnt, int32_t* kv_idx,
+                     int32_t* sel_cnt, int32_t* sel_idx, int32_t* const* kv_cnt, int32_t* const* kv_idx,
                      void* stream) {
     int rc = check_geom(geom);
     if (rc) return rc;
-    if (d_scale < 0 || t_scale < d_scale || t_scale >= geom->n_scales) return VARSPARSE_EINVAL;
-    if (geom->side[d_scale] % geom->tile != 0 || geom->side[t_scale] % geom->tile != 0) return VARSPARSE_EINVAL;
+    if (n_targets < 1 || n_targets > vs::kMaxTargets || t_scales == nullptr) return VARSPARSE_EINVAL;
+    if (kv_cnt == nullptr || kv_idx == nullptr) return VARSPARSE_EINVAL;
+    if (d_scale < 0 || d_scale >= geom->n_scales || geom->side[d_scale] % geom->tile != 0) return VARSPARSE_EINVAL;
+    int t_max = d_scale;
+    for (int i = 0; i < n_targets; ++i) {
+        const int T = t_scales[i];
+        if (T < d_scale || T >= geom->n_scales || geom->side[T] % geom->tile != 0) return VARSPARSE_EINVAL;
+        if (kv_cnt[i] == nullptr || kv_idx[i] == nullptr) return VARSPARSE_EINVAL;
+        t_max = std::max(t_max, T);
+    }
     if (n_sink < 0 || n_sink > d_scale) return VARSPARSE_EINVAL;
     if (!(top_p > 0.0f && top_p <= 1.0f)) return VARSPARSE_EINVAL;
     if (B < 1 || H < 1) return VARSPARSE_EINVAL;
-    if (scores == nullptr || kv_cnt == nullptr || kv_idx == nullptr) return VARSPARSE_EINVAL;
+    if (scores == nullptr) return VARSPARSE_EINVAL;
     if ((sel_cnt == nullptr) != (sel_idx == nullptr)) return VARSPARSE_EINVAL;
     const vs::DevGeom gD = vs::make_dev_geom(*geom, d_scale);
-    const vs::DevGeom gT = vs::make_dev_geom(*geom, t_scale);
+    const vs::DevGeom gT = vs::make_dev_geom(*geom, t_max);
     const int nqbD = gD.nb[d_scale] * gD.nb[d_scale], nkbD = gD.tile_base[d_scale + 1];
-    const int nqbT = gT.nb[t_scale] * gT.nb[t_scale], nkbT = gT.tile_base[t_scale + 1];
     if (nkbD > 240) return VARSPARSE_EUNSUPPORTED;
-    const int words = (nkbD + 31) / 32;
-    if ((int64_t)B * H * std::max(nqbD, (nqbT + 3) / 4) > 0x7fffffff) return VARSPARSE_EINVAL;
+    vs::SelMapArgs m{};
+    m.n_targets = n_targets;
+    int64_t groups = 0;
+    for (int i = 0; i < n_targets; ++i) {
+        const int T = t_scales[i];
+        m.t_scale[i] = T;
+        m.nqbT[i] = gT.nb[T] * gT.nb[T];
+        m.nkbT[i] = gT.tile_base[T + 1];
+        m.group_base[i] = (int32_t)groups;
+        m.kv_cnt[i] = kv_cnt[i];
+        m.kv_idx[i] = kv_idx[i];
+        groups += (m.nqbT[i] + 3) / 4;
+    }
+    m.group_base[n_targets] = (int32_t)groups;
+    if ((int64_t)B * H * std::max<int64_t>(nqbD, groups) > 0x7fffffff) return VARSPARSE_EINVAL;
+    m.groups_total = (int32_t)groups;
     if (q_d != nullptr) {
         if (dtype != VARSPARSE_BF16) return VARSPARSE_EUNSUPPORTED;
         if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;
@@ -158,16 +179,12 @@ int map_indices_impl(const varsparse_geom* geom, int32_t d_scale, int32_t t_scal
         rc = hip_status(vs::launch_cs4a_score(sa, head_dim, (hipStream_t)stream));
         if (rc) return rc;
     }
-    vs::SelMapArgs m{};
     m.g = gT;
     m.d_scale = d_scale;
-    m.t_scale = t_scale;
     m.n_sink = n_sink;
     m.nqbD = nqbD;
     m.nkbD = nkbD;
-    m.nqbT = nqbT;
-    m.nkbT = nkbT;
-    m.words = words;
+    m.words = (nkbD + 31) / 32;
     m.rule = rule;
     // Top-K: ceil of the float32 product frac * nkb_D, clamped to [1, nkb_D]
     m.k_keep = std::min(std::max((int)ceilf(top_p * (float)nkbD), 1), nkbD);
@@ -175,8 +192,6 @@ int map_indices_impl(const varsparse_geom* geom, int32_t d_scale, int32_t t_scal
     m.scores = scores;
     m.sel_cnt = sel_cnt;
     m.sel_idx = sel_idx;
-    m.kv_cnt = kv_cnt;
-    m.kv_idx = kv_idx;
     return hip_status(vs::launch_cs4a_select_map(m, B * H, (hipStream_t)stream));
 }
 
@@ -190,8 +205,8 @@ int varsparse_map_indices(const varsparse_geom* geom, int32_t d_scale, int32_t t
                           const int64_t k_strides[3], float softmax_scale, float* scores,
                           int32_t* sel_cnt, int32_t* sel_idx, int32_t* kv_cnt, int32_t* kv_idx,
                           void* stream) {
-    return map_indices_impl(geom, d_scale, t_scale, n_sink, 0, top_p, dtype, B, H, head_dim, q_d, q_strides, k,
-                            k_strides, softmax_scale, scores, sel_cnt, sel_idx, kv_cnt, kv_idx, stream);
+    return map_indices_impl(geom, d_scale, 1, &t_scale, n_sink, 0, top_p, dtype, B, H, head_dim, q_d, q_strides,
+                            k, k_strides, softmax_scale, scores, sel_cnt, sel_idx, &kv_cnt, &kv_idx, stream);
 }
 
 int varsparse_map_indices_topk(const varsparse_geom* geom, int32_t d_scale, int32_t t_scale, int32_t n_sink,
@@ -200,8 +215,21 @@ int varsparse_map_indices_topk(const varsparse_geom* geom, int32_t d_scale, int3
                                const int64_t k_strides[3], float softmax_scale, float* scores,
                                int32_t* sel_cnt, int32_t* sel_idx, int32_t* kv_cnt, int32_t* kv_idx,
                                void* stream) {
-    return map_indices_impl(geom, d_scale, t_scale, n_sink, 1, top_k_frac, dtype, B, H, head_dim, q_d, q_strides,
-                            k, k_strides, softmax_scale, scores, sel_cnt, sel_idx, kv_cnt, kv_idx, stream);
+    return map_indices_impl(geom, d_scale, 1, &t_scale, n_sink, 1, top_k_frac, dtype, B, H, head_dim, q_d,
+                            q_strides, k, k_strides, softmax_scale, scores, sel_cnt, sel_idx, &kv_cnt, &kv_idx,
+                            stream);
+}
+
+int varsparse_map_indices_multi(const varsparse_geom* geom, int32_t d_scale, int32_t n_targets,
+                                const int32_t* t_scales, int32_t n_sink, int32_t rule, float param,
+                                varsparse_dtype dtype, int32_t B, int32_t H, int32_t head_dim,
+                                const void* q_d, const int64_t q_strides[3], const void* k,
+                                const int64_t k_strides[3], float softmax_scale, float* scores,
+                                int32_t* const* kv_cnt, int32_t* const* kv_idx, void* stream) {
+    if (rule != VARSPARSE_SELECT_TOP_P && rule != VARSPARSE_SELECT_TOP_K) return VARSPARSE_EINVAL;
+    return map_indices_impl(geom, d_scale, n_targets, t_scales, n_sink, rule, param, dtype, B, H, head_dim, q_d,
+                            q_strides, k, k_strides, softmax_scale, scores, nullptr, nullptr, kv_cnt, kv_idx,
+                            stream);
 }
 
 int varsparse_attn_fwd(const varsparse_geom* geom, int32_t q_scale, varsparse_dtype dtype, int32_t B, int32_t H,

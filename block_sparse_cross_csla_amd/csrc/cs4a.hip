@@ -13,7 +13,8 @@
 // LDS ahead of use.  Reductions run in a fixed order: scores are
 // bit-reproducible.
 //
-// cs4a_select_map_kernel: one wave per (batch, head, target query tile).
+// cs4a_select_map_kernel: one wave per (batch, head, target scale, target
+// query tile); one launch maps the selection onto up to kMaxTargets scales.
 // Top-p (or Top-K) on integer-quantised scores (exact, associative) of the
 // parent decision tile, kept as a bitset in registers, then the target-scale lists: parent tile by floor scaling, tiles below the
 // decision scale copied, decision-scale tiles expanded to their footprint on
@@ -243,13 +244,17 @@ __device__ __forceinline__ int64_t quantise(float s) {
 __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a) {
     __shared__ int64_t mq[4][256];   // quantised scores of each wave's parent tile
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int groups = (a.nqbT + 3) / 4;
-    const int bh = blockIdx.x / groups;
-    const int qt = (blockIdx.x - bh * groups) * 4 + wave;
-    if (qt >= a.nqbT) return;   // whole wave leaves; no workgroup barrier below
+    // block -> (b h, target, group of 4 target query tiles)
+    const int bh = blockIdx.x / a.groups_total;
+    const int gi = blockIdx.x - bh * a.groups_total;
+    int tg = 0;
+    while (tg + 1 < a.n_targets && a.group_base[tg + 1] <= gi) ++tg;
+    const int T = a.t_scale[tg], nqbT = a.nqbT[tg], nkbT = a.nkbT[tg];
+    const int qt = (gi - a.group_base[tg]) * 4 + wave;
+    if (qt >= nqbT) return;   // whole wave leaves; no workgroup barrier below
     const int nkbD = a.nkbD;
     const int D = a.d_scale, t = a.g.tile;
-    const int hD = a.g.side[D], nbD = a.g.nb[D], nbT = a.g.nb[a.t_scale];
+    const int hD = a.g.side[D], nbD = a.g.nb[D], nbT = a.g.nb[T];
     const int ti = qt / nbT, tj = qt - ti * nbT;
     const int pi = ti * nbD / nbT, pj = tj * nbD / nbT;
     const int parent = pi * nbD + pj;
@@ -286,7 +291,7 @@ __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a
     }
     const bool first_row = ti == 0 || (ti - 1) * nbD / nbT != pi;
     const bool first_col = tj == 0 || (tj - 1) * nbD / nbT != pj;
-    if (a.sel_idx != nullptr && first_row && first_col) {
+    if (a.sel_idx != nullptr && tg == 0 && first_row && first_col) {
         int base = 0;
         int32_t* out = a.sel_idx + ((int64_t)bh * a.nqbD + parent) * nkbD;
 #pragma unroll
@@ -317,8 +322,8 @@ __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // this wave's LDS writes before its reads
     int base = 0;
-    int32_t* out = a.kv_idx + ((int64_t)bh * a.nqbT + qt) * a.nkbT;
-    for (int s = 0; s <= a.t_scale; ++s) {
+    int32_t* out = a.kv_idx[tg] + ((int64_t)bh * nqbT + qt) * nkbT;
+    for (int s = 0; s <= T; ++s) {
         const int tb0 = a.g.tile_base[s], tb1 = a.g.tile_base[s + 1];
         const int hs = a.g.side[s], nbs = a.g.nb[s];
         if (s >= D) {
@@ -361,8 +366,8 @@ __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a
             base += __popcll(bal);
         }
     }
-    for (int j = base + lane; j < a.nkbT; j += 64) out[j] = -1;
-    if (lane == 0) a.kv_cnt[(int64_t)bh * a.nqbT + qt] = base;
+    for (int j = base + lane; j < nkbT; j += 64) out[j] = -1;
+    if (lane == 0) a.kv_cnt[tg][(int64_t)bh * nqbT + qt] = base;
 }
 
 hipError_t launch_cs4a_score(const ScoreArgs& a, int head_dim, hipStream_t stream) {
@@ -385,8 +390,7 @@ hipError_t launch_cs4a_score(const ScoreArgs& a, int head_dim, hipStream_t strea
 }
 
 hipError_t launch_cs4a_select_map(const SelMapArgs& a, int bh, hipStream_t stream) {
-    const int groups = (a.nqbT + 3) / 4;
-    hipLaunchKernelGGL(cs4a_select_map_kernel, dim3(bh * groups), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(cs4a_select_map_kernel, dim3(bh * a.groups_total), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -66,17 +66,23 @@ struct ScoreArgs {
     DevGeom g;   // scales 0..D
 };
 
+constexpr int kMaxTargets = 8;   // target scales mapped by one select/map launch
+
 struct SelMapArgs {
-    DevGeom g;   // scales 0..T
-    int32_t d_scale, t_scale, n_sink, nqbD, nkbD, nqbT, nkbT, words;
+    DevGeom g;   // scales 0..largest target
+    int32_t d_scale, n_sink, nqbD, nkbD, words;
     int32_t rule;     // 0: top-p (top_p), 1: Top-K fraction (k_keep tiles)
     int32_t k_keep;
     double top_p;
     const float* scores;
-    int32_t* sel_cnt;
+    int32_t* sel_cnt;   // written by target 0's waves when non-null
     int32_t* sel_idx;
-    int32_t* kv_cnt;
-    int32_t* kv_idx;
+    int32_t n_targets;
+    int32_t groups_total;                   // sum over targets of ceil(nqbT / 4)
+    int32_t t_scale[kMaxTargets], nqbT[kMaxTargets], nkbT[kMaxTargets];
+    int32_t group_base[kMaxTargets + 1];    // prefix sums of ceil(nqbT / 4)
+    int32_t* kv_cnt[kMaxTargets];
+    int32_t* kv_idx[kMaxTargets];
 };
 
 struct OcacheArgs {

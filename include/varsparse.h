@@ -202,6 +202,32 @@ int varsparse_attn_fwd(const varsparse_geom* geom, int32_t q_scale, varsparse_dt
                        const int32_t* kv_cnt, const int32_t* kv_idx, int32_t lists_per_head,
                        void* stream);
 
+/* Selection rule of varsparse_map_indices_multi. */
+enum {
+    VARSPARSE_SELECT_TOP_P = 0,   /* param = p, as varsparse_map_indices       */
+    VARSPARSE_SELECT_TOP_K = 1    /* param = fraction, as varsparse_map_indices_topk */
+};
+
+/*
+ * CS4A scoring, selection and index mapping onto several target scales in one
+ * launch (SparVAR, ai.info summary, "Methodology in Plain English", first
+ * module: the indices selected at the decision scale are mapped to the later
+ * scales; all of them depend only on the decision scale, so they are built
+ * together right after it).  For each i < n_targets the lists of target
+ * scale t_scales[i] are exactly those varsparse_map_indices (rule 0) or
+ * varsparse_map_indices_topk (rule 1) writes for that target: kv_cnt[i] dev
+ * int32 [B*H*nqb_T], kv_idx[i] dev int32 [B*H*nqb_T*nkb_T].  kv_cnt, kv_idx,
+ * t_scales: host arrays of n_targets entries (1 <= n_targets <= 8), each
+ * target d_scale <= t < n_scales.  Scores as in varsparse_map_indices
+ * (computed when q_d is non-NULL, else read).  No selection output.
+ */
+int varsparse_map_indices_multi(const varsparse_geom* geom, int32_t d_scale, int32_t n_targets,
+                                const int32_t* t_scales, int32_t n_sink, int32_t rule, float param,
+                                varsparse_dtype dtype, int32_t B, int32_t H, int32_t head_dim,
+                                const void* q_d, const int64_t q_strides[3], const void* k,
+                                const int64_t k_strides[3], float softmax_scale, float* scores,
+                                int32_t* const* kv_cnt, int32_t* const* kv_idx, void* stream);
+
 /*
  * Block-sparse attention with 128-query workgroups (SparVAR, ai.info
  * summary, "Main Findings": the block-wise kernel measured with blocks of

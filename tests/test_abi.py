@@ -224,3 +224,25 @@ def test_attn_pair_validation():
     assert call(q=13) == _lib.EINVAL
     big = (8, 16, 32, 64, 128, 256, 512)                      # 5461 key tiles
     assert call(g=_g(big), q=6) == _lib.EUNSUPPORTED
+
+
+def test_map_indices_multi_validation():
+    lib = _lib.lib()
+    p = ctypes.c_void_p(1 << 20)
+    ptrs = (ctypes.c_void_p * 3)(p, p, p)
+    nulls = (ctypes.c_void_p * 3)(p, None, p)
+
+    def call(d=9, ts=(10, 11, 12), n=None, sink=5, rule=0, param=0.9, cnts=ptrs, idxs=ptrs, scores=p):
+        n = len(ts) if n is None else n
+        t = (ctypes.c_int32 * max(len(ts), 1))(*ts)
+        return lib.varsparse_map_indices_multi(_g(), d, n, t, sink, rule, param, _lib.BF16, 2, 16, 128, None, None,
+                                               None, None, 0.088, scores, cnts, idxs, None)
+    assert call(n=0) == _lib.EINVAL
+    assert call(n=9) == _lib.EINVAL                      # at most eight targets
+    assert call(ts=(8, 11, 12)) == _lib.EINVAL           # a target below the decision scale
+    assert call(ts=(10, 13, 12)) == _lib.EINVAL          # a target past the schedule
+    assert call(rule=2) == _lib.EINVAL
+    assert call(param=0.0) == _lib.EINVAL
+    assert call(cnts=nulls) == _lib.EINVAL
+    assert call(scores=None) == _lib.EINVAL
+    assert call(sink=10) == _lib.EINVAL

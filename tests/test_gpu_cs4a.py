@@ -179,3 +179,42 @@ def test_large_decision_scale():
     assert (sc.cpu().numpy() == cnt).all() and (si.cpu().numpy() == idx).all()
     mc, mi = OC.map_indices(cnt, idx, w.sides, D, T, w.tile, w.n_sink)
     assert (kc.cpu().numpy() == mc).all() and (ki.cpu().numpy() == mi).all()
+
+
+@pytest.mark.parametrize("rule,param", [("top_p", W.CS4A_TOP_P), ("top_k", 0.2)])
+def test_multi_target_map_bit_exact(cs4a_run, rule, param):
+    """One launch mapping onto the decision scale itself and the three targets
+    writes exactly the lists of one launch per target, and those equal the
+    oracle's select/map of the GPU's own scores."""
+    vs = _vs()
+    r = cs4a_run
+    w = r["w"]
+    D = r["D"]
+    targets = [D, *W.CS4A_TARGETS]
+    scores = torch.from_numpy(r["scores"]).cuda()
+    _, multi = vs.map_indices_multi(w.sides, w.tile, D, targets, w.n_sink, param, rule=rule, scores=scores)
+    torch.cuda.synchronize()
+    s = r["scores"]
+    cnt, idx = OC.top_p_select(s, param) if rule == "top_p" else OC.top_k_select(s, param)
+    for T, (kc, ki) in zip(targets, multi):
+        kw = {"top_k": param} if rule == "top_k" else {}
+        one = vs.map_indices(w.sides, w.tile, D, T, w.n_sink, W.CS4A_TOP_P, scores=scores, **kw)[3:]
+        torch.cuda.synchronize()
+        assert torch.equal(kc, one[0]) and torch.equal(ki, one[1]), T
+        mc, mi = OC.map_indices(cnt, idx, w.sides, D, T, w.tile, w.n_sink)
+        assert (kc.cpu().numpy() == mc).all() and (ki.cpu().numpy() == mi).all(), T
+
+
+def test_multi_target_map_computes_scores():
+    """With q_d and k the multi-target launch computes the scores first, as
+    the single-target entry point does (identical scores and lists)."""
+    vs = _vs()
+    w = W.CS4A
+    D = W.CS4A_DECISION
+    q_d, k, _ = spatial(w, B=2, H=4, q_side=w.sides[D])
+    qd, kd = to_device(q_d), to_device(k)
+    s1, multi = vs.map_indices_multi(w.sides, w.tile, D, list(W.CS4A_TARGETS), w.n_sink, W.CS4A_TOP_P, q_d=qd, k=kd)
+    s2, _, _, kc, ki = vs.map_indices(w.sides, w.tile, D, W.CS4A_TARGETS[-1], w.n_sink, W.CS4A_TOP_P, q_d=qd, k=kd)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(multi[-1][0], kc) and torch.equal(multi[-1][1], ki)
