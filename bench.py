@@ -128,23 +128,42 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    # timed region: K whole steps, HIP events around every launch on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Mean launch duration of one kernel: reps back-to-back launches on the
+    # launch stream, HIP events around the whole run (an event between two
+    # launches would put a timing packet, and its cache flush, between them).
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    # timed region: K whole steps (mask + attention) bracketed by device
+    # synchronisations; HIP events only at its two ends
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, radius=w.radii, out=(kv_cnt, kv_idx, None), stream=stream)
-        ev[i][1].record(stream)
-        vs.attn_fwd(q, k, v, w.sides, w.tile, w.q_scale, kv_cnt, kv_idx, softmax_scale=scale, out=o, lse=lse,
-                    stream=stream)
-        ev[i][2].record(stream)
+    e_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    mask_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]))
-    attn_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]))
-    print(f"[bench] sparse steps done: {ms_step:.4f} ms/step, attn {attn_ms:.4f} ms", file=sys.stderr, flush=True)
+    gpu_ms_step = e_start.elapsed_time(e_end) / args.steps
+    print(f"[bench] sparse steps done: {ms_step:.4f} ms/step (events {gpu_ms_step:.4f})", file=sys.stderr, flush=True)
+
+    # each kernel of the step alone, same lists and tensors
+    attn_ms = timed(lambda: vs.attn_fwd(q, k, v, w.sides, w.tile, w.q_scale, kv_cnt, kv_idx, softmax_scale=scale,
+                                        out=o, lse=lse, stream=stream), args.steps)
+    mask_ms = timed(lambda: vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, radius=w.radii,
+                                          out=(kv_cnt, kv_idx, None), stream=stream), args.steps)
+    print(f"[bench] kernels alone: attn {attn_ms:.4f} ms, mask {mask_ms:.4f} ms", file=sys.stderr, flush=True)
 
     sizes = tile_sizes(w.sides, w.q_scale, w.tile)
     cnt_h, idx_h = kv_cnt.cpu().numpy(), kv_idx.cpu().numpy()
@@ -155,33 +174,12 @@ def main():
 
     # dense comparator on the same tensors
     nd = max(3, args.steps // 5)
-    for _ in range(2):
-        vs.dense_attn_fwd(q, k, v, softmax_scale=scale, out=od, lse=lsed, stream=stream)
-    torch.cuda.synchronize()
-    de = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nd)]
-    for i in range(nd):
-        de[i][0].record(stream)
-        vs.dense_attn_fwd(q, k, v, softmax_scale=scale, out=od, lse=lsed, stream=stream)
-        de[i][1].record(stream)
-    torch.cuda.synchronize()
-    dense_ms = float(np.mean([de[i][0].elapsed_time(de[i][1]) for i in range(nd)]))
+    dense_ms = timed(lambda: vs.dense_attn_fwd(q, k, v, softmax_scale=scale, out=od, lse=lsed, stream=stream), nd)
     print(f"[bench] dense done: {dense_ms:.4f} ms", file=sys.stderr, flush=True)
 
     # token-level CSLA on the same tensors: the token-masked dense baseline
     # (every key tile, the token rule applied) and token-exact block-sparse
     # attention (the CSLA tiles, the token rule inside them)
-    def timed(fn, reps):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-        for e in evs:
-            e[0].record(stream)
-            fn()
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-
     tok_dense_ms = timed(lambda: vs.attn_fwd_token(q, k, v, w.sides, w.tile, w.q_scale, w.n_sink, w.radii,
                                                    softmax_scale=scale, out=od, lse=lsed, stream=stream), nd)
     tok_sparse_ms = timed(lambda: vs.attn_fwd_token(q, k, v, w.sides, w.tile, w.q_scale, w.n_sink, w.radii, kv_cnt, kv_idx,
@@ -207,6 +205,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "gpu_ms_per_step": gpu_ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
