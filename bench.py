@@ -33,7 +33,7 @@ PEAK_HBM_GBS = 8000.0
 # rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by a 256 MiB copy
 # (x2.000 and x1.000), recorded with the SHA-256 of the kernel sources they
 # were taken on; reported only while those sources are unchanged.
-TRAFFIC = {"bytes": 366.5e6, "sources_sha256": "4fbafd19980b174efe28cfdfc6f708c9b5e86676f49d7d9d840cac8657c40604"}
+TRAFFIC = {"bytes": 370.2e6, "sources_sha256": "4fbafd19980b174efe28cfdfc6f708c9b5e86676f49d7d9d840cac8657c40604"}
 KERNEL_SOURCES = ("block_sparse_cross_csla_amd/csrc/attn_bf16.hip", "block_sparse_cross_csla_amd/csrc/common.h",
                   "block_sparse_cross_csla_amd/csrc/kernel_args.h")
 
@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cs4a", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-single", action="store_true",
+                   help="skip the single-launch warm/cold timings (keeps counter runs to back-to-back launches)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -165,6 +167,34 @@ def main():
                                           out=(kv_cnt, kv_idx, None), stream=stream), args.steps)
     print(f"[bench] kernels alone: attn {attn_ms:.4f} ms, mask {mask_ms:.4f} ms", file=sys.stderr, flush=True)
 
+    # single launches, warm and cold: HIP events around one attention launch,
+    # median over runs; cold = a 512 MiB scrub buffer written before each launch
+    # (more than the L2s and the MALL hold, so K, V and Q come from HBM)
+    def single_launch_median(runs, scrub=None):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(runs)]
+        for i, e in enumerate(evs):
+            if scrub is not None:
+                scrub.fill_(i & 0xff)
+            e[0].record(stream)
+            vs.attn_fwd(q, k, v, w.sides, w.tile, w.q_scale, kv_cnt, kv_idx, softmax_scale=scale, out=o, lse=lse,
+                        stream=stream)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+
+    single = None
+    if not args.no_single:
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        n_single = max(10, min(100, args.steps))
+        warm_single_ms = single_launch_median(n_single)
+        cold_single_ms = single_launch_median(max(10, n_single // 3), scrub)
+        del scrub
+        single = {"warm_median_ms": warm_single_ms, "cold_median_ms": cold_single_ms,
+                  "cold_tflops": None, "runs": [n_single, max(10, n_single // 3)],
+                  "what": "HIP events around one launch, median; cold: 512 MiB scrub written before each"}
+        print(f"[bench] single launches: warm {warm_single_ms:.4f} ms, cold {cold_single_ms:.4f} ms",
+              file=sys.stderr, flush=True)
+
     sizes = tile_sizes(w.sides, w.q_scale, w.tile)
     cnt_h, idx_h = kv_cnt.cpu().numpy(), kv_idx.cpu().numpy()
     flops = kept_flops(cnt_h, idx_h, sizes, w.tile * w.tile, w.d, w.B * w.H)
@@ -228,13 +258,19 @@ def main():
         "block128_pair": {"ms": pair_ms, "ms_64_query_kernel": ref64_ms, "flop_per_launch": flops,
                           "tflops": flops / (pair_ms * 1e-3) / 1e12, "vs_64_query_kernel": ref64_ms / pair_ms,
                           "what": "128-query workgroups over pairs of 8x8 query tiles, union chunk walk"},
+        "single_launch": single,
         "roofline": {"bound": "mfma", "achieved": flops / (attn_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                      "traffic": TRAFFIC["bytes"] if kernel_sources_sha256() == TRAFFIC["sources_sha256"] else None,
-                     "traffic_unit": "bytes per launch", "kernel": "attn_fwd_bf16_kernel<128,false,false>",
+                     "traffic_unit": "bytes per launch",
+                     "traffic_tb_per_s": (TRAFFIC["bytes"] / (attn_ms * 1e-3) / 1e12
+                                          if kernel_sources_sha256() == TRAFFIC["sources_sha256"] else None),
+                     "kernel": "attn_fwd_bf16_kernel<128,false,false>",
                      "flop_per_launch": flops},
     }
 
+    if single is not None:
+        single["cold_tflops"] = flops / (single["cold_median_ms"] * 1e-3) / 1e12
     if args.copy_probe:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
