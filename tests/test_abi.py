@@ -92,6 +92,11 @@ def test_attn_validation():
     assert call(g=_g(SCHEDULE_13, 4)) == _lib.EUNSUPPORTED    # bf16 MFMA path uses 8x8 tiles
     assert call(g=_g(TINY_SIDES, 16), q=4, dt=_lib.FP32, d=64) == _lib.EUNSUPPORTED
     assert call(dt=7) == _lib.EINVAL
+    # K or V rows 2^20 elements apart over 10521 cached tokens: byte offsets past
+    # 2^31, which the bf16 kernels cannot address (32-bit per-head offsets)
+    far = 1 << 20
+    assert call(st=[0, 0, 128, 0, 0, far, 0, 0, 128, 0, 0, 128]) == _lib.EUNSUPPORTED
+    assert call(st=[0, 0, 128, 0, 0, 128, 0, 0, far, 0, 0, 128]) == _lib.EUNSUPPORTED
     assert call(B=0) == _lib.EINVAL
     assert call(scale=0.0) == _lib.EINVAL
     assert call(scale=float("nan")) == _lib.EINVAL
