@@ -201,6 +201,31 @@ def test_full_size_high_res_sampled():
     _compare(o, lse, ro, rl, BF16_TOL, "high-res")
 
 
+@pytest.mark.parametrize("w", [W.LAST_TWO_8B_48, W.LAST_TWO_8B_64], ids=lambda w: w.name)
+def test_full_size_budget_sweep_sampled(w):
+    """The budget-sweep shape (B=2, H=28: 56 heads, a launch whose workgroups
+    fill the chip 3.5 times at side 64) at each budget of the sweep
+    (75/85/90/95% block sparsity): sampled query tiles of first, middle and
+    last heads against the oracle, on the oracle's own budget lists."""
+    vs = _vs()
+    q, k, v = spatial(w)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    nqb = (w.sides[w.q_scale] // w.tile) ** 2
+    tiles = sorted({0, 5, nqb // 2, nqb - 1})
+    bh = [(0, 0), (1, 13), (1, 27)]
+    for budget in w.budgets:
+        print(f"budget sweep {w.name} budget={budget}", flush=True)
+        cnt, idx, _ = vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, budget=budget)
+        o, lse = vs.attn_fwd(qd, kd, vd, w.sides, w.tile, w.q_scale, cnt, idx)
+        torch.cuda.synchronize()
+        mask = oracle_mask(tuple(w.sides), w.q_scale, w.tile, w.n_sink, None, budget)
+        mc, mi = lists(mask)
+        assert np.array_equal(cnt.cpu().numpy(), mc)
+        ro, rl = OA.block_sparse_attention(q, k, v, w.sides, w.q_scale, w.tile, mc, mi, 1 / math.sqrt(w.d),
+                                           q_tiles=tiles, bh=bh)
+        _compare(o, lse, ro, rl, BF16_TOL, f"{w.name} budget {budget}")
+
+
 @pytest.mark.parametrize("per_head", [True, False])
 def test_bf16_eight_heads_every_tile(per_head):
     """B H = 8 (one head per XCD range), shared and per-head random lists of
