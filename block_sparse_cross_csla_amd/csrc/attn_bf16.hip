@@ -375,6 +375,42 @@ __device__ __forceinline__ uint32_t csla_token_bits(TokenState& ts, const Chunk&
     return bits;
 }
 
+// Work item -> (b h, query tile).  Kept lists differ in length (edge tiles
+// of a CSLA window keep fewer key tiles than interior ones), so the launch
+// ends with workgroups of long lists still running on a few slots while the
+// rest of the chip idles.  The items of two consecutive heads are therefore
+// interleaved and each head's query tiles taken in descending list length
+// (ties by tile id): the workgroups dispatched as slots free up take the
+// longest lists first.  Every workgroup ranks the counts of its head itself
+// (one key per lane in LDS, count then tile id: distinct keys, a strict
+// total order), so all agree on one permutation.  Heads with more than 64
+// query tiles, and walks without a list, keep the natural order.
+__device__ __forceinline__ void work_tile(const AttnArgs& a, int work, int nqt, int lane, int* keys, int& bh,
+                                          int& qt) {
+    bh = work / nqt;
+    qt = work - bh * nqt;
+    if (a.kv_cnt == nullptr || nqt > 64) return;
+    const int n_bh = a.B * a.H;
+    const int pair = bh >> 1;
+    const int j = work - 2 * pair * nqt;               // place within the pair's items
+    const bool two = 2 * pair + 1 < n_bh;
+    const int head = two ? 2 * pair + (j & 1) : 2 * pair;
+    const int r = two ? (j >> 1) : j;                  // wanted rank within the head
+    const int32_t* cnt = a.kv_cnt + (a.per_head ? (int64_t)head * a.nqb : 0);
+    // distinct keys, larger = earlier: the count (clamped), then the lower tile id
+    const int key = lane < nqt ? min(max(cnt[lane], 0), (1 << 24) - 1) * 64 + (63 - lane) : -1;
+    keys[lane] = key;
+    int rank = 0;
+#pragma unroll
+    for (int u = 0; u < 64; u += 4) {
+        const int4 k4 = *(const int4*)(keys + u);
+        rank += (k4.x > key) + (k4.y > key) + (k4.z > key) + (k4.w > key);
+    }
+    const uint64_t hit = __ballot(lane < nqt && rank == r);
+    bh = head;
+    qt = __builtin_ctzll(hit);
+}
+
 template <int D, bool DENSE, bool TOKEN>
 __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a) {
     constexpr int KSTEPS = D / 16;
@@ -388,7 +424,16 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
 
     const int64_t nqt = DENSE ? (a.nq + 63) / 64 : a.nqb;
     const int work = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = work / nqt, qt = work - bh * nqt;
+    int bh, qt;
+    if (DENSE) {
+        bh = work / nqt;
+        qt = work - bh * nqt;
+    } else {
+        __shared__ __attribute__((aligned(16))) int rank_keys[2][64];
+        work_tile(a, work, nqt, lane, rank_keys[wave], bh, qt);
+        bh = __builtin_amdgcn_readfirstlane(bh);
+        qt = __builtin_amdgcn_readfirstlane(qt);
+    }
     const int b = bh / a.H, h = bh - b * a.H;
 
     // ---- the query this lane holds (column n of the wave's 32 queries)
