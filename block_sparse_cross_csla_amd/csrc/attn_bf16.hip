@@ -68,13 +68,34 @@ struct Walk {
     const int32_t* idx;
 };
 
+// The geometry of scale `lane` held by that lane (lanes past the last scale:
+// tile_base / tok_off = the totals, then INT_MAX), read once per workgroup:
+// the decoding below takes each scale's figures with readlane instead of a
+// chain of dependent scalar loads from the kernel arguments.
+struct LaneGeom {
+    int32_t tb, off, side, nb;
+};
+
+__device__ __forceinline__ LaneGeom lane_geom(const DevGeom& g, int lane) {
+    LaneGeom lg;
+    const int s = min(lane, kMaxScales - 1);
+    lg.tb = lane <= g.n_scales ? g.tile_base[min(lane, kMaxScales)] : INT_MAX;
+    lg.off = lane <= g.n_scales ? g.tok_off[min(lane, kMaxScales)] : INT_MAX;
+    lg.side = lane < g.n_scales ? g.side[s] : 0;
+    lg.nb = lane < g.n_scales ? g.nb[s] : 1;
+    return lg;
+}
+
 // Wave 0 fills the chunk table with the next descriptors of the walk (the
 // contiguous run first, then tile halves in list order) and returns how many
 // it wrote; list entries are decoded one per lane and placed with a
 // ballot prefix sum (every entry gives 1 or 2 chunks).  Entries are
 // documented to be valid tile ids; out-of-range ids are clamped so that a bad
-// list cannot address outside the cache.
-__device__ __forceinline__ int build_table(Walk& w, const DevGeom& g, uint2* table, int lane) {
+// list cannot address outside the cache.  `first64` holds list entries
+// 0..63 (entry `lane` in lane `lane`, where the list has it) when
+// `have_first64`: entries among them are taken from registers, not memory.
+__device__ __forceinline__ int build_table(Walk& w, const DevGeom& g, const LaneGeom& lg, uint2* table, int lane,
+                                           int first64 = 0, bool have_first64 = false) {
     int n = 0;
     if (w.cnext < w.cend) {
         const int nc = min((w.cend - w.cnext + 31) >> 5, kTableCap);
@@ -85,18 +106,22 @@ __device__ __forceinline__ int build_table(Walk& w, const DevGeom& g, uint2* tab
         w.cnext = min(w.cend, w.cnext + 32 * nc);
         n = nc;
     }
+    const int n_tiles = __builtin_amdgcn_readlane(lg.tb, g.n_scales);
     while (w.j < w.cnt && kTableCap - n >= 128) {
         const int e = w.j + lane;
         const bool valid = e < w.cnt;
-        int id = valid ? (w.idx != nullptr ? w.idx[e] : e) : 0;   // no list: every tile in order
-        id = min(max(id, 0), g.tile_base[g.n_scales] - 1);
-        int tb = 0, side = g.side[0], off = 0, nb = g.nb[0];
+        const int from_regs = __builtin_amdgcn_ds_bpermute((e & 63) << 2, first64);
+        int id = 0;
+        if (valid) id = (have_first64 && e < 64) ? from_regs : (w.idx != nullptr ? w.idx[e] : e);   // no list: every tile
+        id = min(max(id, 0), n_tiles - 1);
+        int tb = 0, side = __builtin_amdgcn_readlane(lg.side, 0), off = 0, nb = __builtin_amdgcn_readlane(lg.nb, 0);
         for (int s = 1; s < g.n_scales; ++s) {
-            if (id >= g.tile_base[s]) {
-                tb = g.tile_base[s];
-                side = g.side[s];
-                off = g.tok_off[s];
-                nb = g.nb[s];
+            const int tbs = __builtin_amdgcn_readlane(lg.tb, s);
+            if (id >= tbs) {
+                tb = tbs;
+                side = __builtin_amdgcn_readlane(lg.side, s);
+                off = __builtin_amdgcn_readlane(lg.off, s);
+                nb = __builtin_amdgcn_readlane(lg.nb, s);
             }
         }
         const int local = id - tb;
@@ -458,11 +483,20 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     const uint32_t lds0 = lds_addr(smem);
     const char* sm = smem;
 
+    // Q^T operands first: their loads are in flight while the walk is set up
+    WaveState<D> st;
+    const __bf16* qp = a.q + b * a.sq_b + h * a.sq_h + tok * a.sq_t;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) st.qreg[s] = *(const bf16x8*)(qp + 16 * s + 8 * g);
+    LoadPlan<D> plan;
+    make_plan<D>(plan, wave, lane, a.sk_t, a.sv_t);
+
     // ---- the walk, in table builds of up to kTableCap chunks (the first one
     // before the accumulators are live)
     Walk w;
     __shared__ int table_n;
     int nch;
+    bool first_loaded = false;   // the first chunk's loads already issued
     if (DENSE) {
         w.cnext = 0;
         w.cend = (int32_t)a.nk;
@@ -470,6 +504,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         w.idx = nullptr;
         nch = (w.cend + 31) >> 5;
     } else {
+        const LaneGeom lg = lane_geom(a.g, lane);
         const int64_t row = (a.per_head ? (int64_t)bh * a.nqb : 0) + qt;
         if (a.kv_cnt != nullptr) {
             w.cnt = a.kv_cnt[row];
@@ -480,9 +515,10 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         }
         // leading run of tiles 0,1,2,...: whole scales kept from the start form
         // one contiguous token range
-        int p = 0;
+        int p = 0, first64 = 0;
         for (;;) {
             const int v = (p + lane < w.cnt) ? (w.idx != nullptr ? w.idx[p + lane] : p + lane) : -1;
+            if (p == 0) first64 = v;
             const uint64_t off = __ballot(v != p + lane);
             if (off) {
                 p += __builtin_ctzll(off);
@@ -490,30 +526,31 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
             }
             p += 64;
         }
-        int s = 0;
-        while (s < a.g.n_scales && a.g.tile_base[s + 1] <= p) ++s;
+        // scales wholly inside the run: those whose tiles all precede tile p
+        int s = __popcll(__ballot(lane >= 1 && lane <= a.g.n_scales && lg.tb <= p));
         if (TOKEN) s = min(s, a.n_sink);   // only sink scales skip the token test
         w.cnext = 0;
-        w.cend = a.g.tok_off[s];
-        w.j = a.g.tile_base[s];
+        w.cend = __builtin_amdgcn_readlane(lg.off, s);
+        w.j = __builtin_amdgcn_readlane(lg.tb, s);
+        // the run's first chunk is known now: its loads overlap the table build
+        if (w.cend > 0) {
+            const int nv = min(32, w.cend);
+            load_chunk<D>(plan, kh, vh, krb, vrb, unpack_chunk(0, pack_info(8, 4, 8, nv)), lds0, lds0 + STAGE, wave,
+                          lane);
+            first_loaded = true;
+        }
         if (wave == 0) {
-            const int nb = build_table(w, a.g, table, lane);
+            const int nb = build_table(w, a.g, lg, table, lane, first64, true);
             if (lane == 0) table_n = nb;
         }
         __syncthreads();   // table visible to both waves
         nch = __builtin_amdgcn_readfirstlane(table_n);
     }
 
-    WaveState<D> st;
-    const __bf16* qp = a.q + b * a.sq_b + h * a.sq_h + tok * a.sq_t;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) st.qreg[s] = *(const bf16x8*)(qp + 16 * s + 8 * g);
 #pragma unroll
     for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] = (f32x16)0.0f;
     st.m_run = -1e30f;   // finite: a fully masked chunk gives P = 0, not NaN
     st.l_run = 0.0f;
-    LoadPlan<D> plan;
-    make_plan<D>(plan, wave, lane, a.sk_t, a.sv_t);
     TokenState ts;
     if (TOKEN) token_init(ts, a, lane);
 
@@ -545,7 +582,8 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         // loads of this chunk in LDS and has finished the previous chunk, whose
         // stage then takes the next prefetch
         Chunk cur = desc(0), nxt;
-        load_chunk<D>(plan, kh, vh, krb, vrb, cur, lds0, lds0 + STAGE, wave, lane);
+        if (!first_loaded) load_chunk<D>(plan, kh, vh, krb, vrb, cur, lds0, lds0 + STAGE, wave, lane);
+        first_loaded = false;
         for (int ci = 0; ci < nch; ci += 2) {
             wait_vmcnt(0);
             wg_barrier();
@@ -570,7 +608,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         // long lists: rebuild the table with what remains of the walk
         __syncthreads();   // every wave done with the table and the stages
         if (wave == 0) {
-            const int nb = build_table(w, a.g, table, lane);
+            const int nb = build_table(w, a.g, lane_geom(a.g, lane), table, lane);
             if (lane == 0) table_n = nb;
         }
         __syncthreads();
