@@ -410,6 +410,9 @@ __device__ __forceinline__ uint32_t csla_token_bits(TokenState& ts, const Chunk&
 // (one key per lane in LDS, count then tile id: distinct keys, a strict
 // total order), so all agree on one permutation.  Heads with more than 64
 // query tiles, and walks without a list, keep the natural order.
+// PAIRS: the items are pairs of query tiles (2i, 2i + 1), ranked by the sum of
+// their two list lengths.
+template <bool PAIRS = false>
 __device__ __forceinline__ void work_tile(const AttnArgs& a, int work, int nqt, int lane, int* keys, int& bh,
                                           int& qt) {
     bh = work / nqt;
@@ -422,8 +425,17 @@ __device__ __forceinline__ void work_tile(const AttnArgs& a, int work, int nqt, 
     const int head = two ? 2 * pair + (j & 1) : 2 * pair;
     const int r = two ? (j >> 1) : j;                  // wanted rank within the head
     const int32_t* cnt = a.kv_cnt + (a.per_head ? (int64_t)head * a.nqb : 0);
-    // distinct keys, larger = earlier: the count (clamped), then the lower tile id
-    const int key = lane < nqt ? min(max(cnt[lane], 0), (1 << 24) - 1) * 64 + (63 - lane) : -1;
+    // distinct keys, larger = earlier: the list length (clamped), then the lower item id
+    int len = 0;
+    if (lane < nqt) {
+        if (PAIRS) {
+            len = max(cnt[2 * lane], 0);
+            if (2 * lane + 1 < a.nqb) len += max(cnt[2 * lane + 1], 0);
+        } else {
+            len = max(cnt[lane], 0);
+        }
+    }
+    const int key = lane < nqt ? min(len, (1 << 24) - 1) * 64 + (63 - lane) : -1;
     keys[lane] = key;
     int rank = 0;
 #pragma unroll
@@ -793,7 +805,11 @@ __global__ __launch_bounds__(256, 2) void attn_pair_bf16_kernel(const AttnArgs a
 
     const int npair = (a.nqb + 1) >> 1;
     const int work = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = work / npair, pr = work - bh * npair;
+    __shared__ __attribute__((aligned(16))) int rank_keys[4][64];
+    int bh, pr;
+    work_tile<true>(a, work, npair, lane, rank_keys[wave], bh, pr);   // pairs with the longest lists first
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    pr = __builtin_amdgcn_readfirstlane(pr);
     const int b = bh / a.H, h = bh - b * a.H;
     const int qt = 2 * pr + tile_sel;
     const bool tile_ok = qt < a.nqb;                         // the pair of an odd last tile has one tile
