@@ -20,15 +20,18 @@
 namespace vs {
 
 // Gap between the projected query rows of query-tile row qi and the rows of
-// key-tile row ka of a scale of side h (0 if they overlap).
-__device__ __forceinline__ int64_t row_gap(int qi, int ka, int t, int h, int H) {
-    const int64_t lo = ((int64_t)qi * t * h) / H;
-    const int64_t hi = ((int64_t)(qi * t + t - 1) * h) / H;
-    const int64_t klo = (int64_t)ka * t, khi = (int64_t)min(ka * t + t, h) - 1;
-    return max((int64_t)0, max(klo - hi, lo - khi));
+// key-tile row ka of a scale of side h (0 if they overlap).  The geometry
+// keeps the total token count below 2^30, so every side is below 2^15 and
+// (qi t + t - 1) h < H h < 2^30: the products and quotients are exact in 32
+// bits (unsigned division, far cheaper than 64-bit division on the GPU).
+__device__ __forceinline__ int row_gap(int qi, int ka, int t, int h, int H) {
+    const int lo = (int)((uint32_t)(qi * t) * (uint32_t)h / (uint32_t)H);
+    const int hi = (int)((uint32_t)(qi * t + t - 1) * (uint32_t)h / (uint32_t)H);
+    const int klo = ka * t, khi = min(ka * t + t, h) - 1;
+    return max(0, max(klo - hi, lo - khi));
 }
 
-__device__ __forceinline__ int64_t tile_gap(const DevGeom& g, int s, int local, int ti, int tj, int H) {
+__device__ __forceinline__ int tile_gap(const DevGeom& g, int s, int local, int ti, int tj, int H) {
     const int nb = g.nb[s], t = g.tile, h = g.side[s];
     const int a = local / nb, b = local - a * nb;
     return max(row_gap(ti, a, t, h, H), row_gap(tj, b, t, h, H));
