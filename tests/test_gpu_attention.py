@@ -272,3 +272,39 @@ def test_bf16_large_scores_lazy_rescale(gain):
     rows = np.arange(0, nq, 37)
     rdo, rdl = OA.dense_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), scale, q_rows=rows)
     _compare(od, lsed, rdo, rdl, BF16_TOL, f"large scores dense gain={gain}")
+
+
+def test_odd_head_count_every_tile_all_list_kernels():
+    """B=1, H=3: the dispatch order interleaves the work items of head pairs
+    and ranks each head's query tiles by list length, so the last pair holds
+    a single head.  Per-head random lists whose lengths differ from tile to
+    tile (an empty row in the lone head, a full row): every query tile of
+    every head against the oracle for the 64-query and the paired-tile
+    kernels; token-exact attention over the shared CSLA lists, three heads."""
+    vs = _vs()
+    sides, qs, t = SCHEDULE_13, 10, 8            # side 40: 25 query tiles, 72 key tiles
+    B, H, d = 1, 3, 128
+    scale = 1 / math.sqrt(d)
+    nqb, nkb, nq, nk = G.counts(sides, qs, t)
+    rng = np.random.default_rng(41)
+    keep = rng.random((B, H, nqb, nkb)) < rng.choice([0.05, 0.2, 0.5, 0.9], size=(B, H, nqb, 1))
+    keep[0, 2, 3] = False
+    keep[0, 0, 7] = True
+    cnt, idx = lists(keep)
+    q, k, v = gaussian(8, 81, B, H, nq, nk, d)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    q64, k64, v64 = q.astype(np.float64), k.astype(np.float64), v.astype(np.float64)
+    ro, rl = OA.block_sparse_attention(q64, k64, v64, sides, qs, t, cnt, idx, scale)
+    cd, idd = torch.from_numpy(cnt).cuda(), torch.from_numpy(idx).cuda()
+    for name, fn in (("64-query", vs.attn_fwd), ("paired", vs.attn_fwd_pair)):
+        print(f"odd heads: {name}", flush=True)
+        o, lse = fn(qd, kd, vd, sides, t, qs, cd, idd)
+        torch.cuda.synchronize()
+        _compare(o, lse, ro, rl, BF16_TOL, f"odd heads {name}")
+        assert (o[0, 2, G.query_tiles(sides, qs, t)[3].tokens()].float() == 0).all()
+    n_sink, rad = 5, [2] * (qs + 1)
+    mc, mi, _ = vs.build_mask(sides, t, qs, n_sink, radius=rad)
+    o, lse = vs.attn_fwd_token(qd, kd, vd, sides, t, qs, n_sink, rad, mc, mi)
+    torch.cuda.synchronize()
+    ro, rl = OA.token_masked_attention(q64, k64, v64, sides, qs, t, n_sink, rad, scale)
+    _compare(o, lse, ro, rl, BF16_TOL, "odd heads token-exact")
