@@ -226,6 +226,199 @@ __global__ __launch_bounds__(kScoreThreads) void cs4a_score_kernel(const ScoreAr
     }
 }
 
+// Two decision query tiles per workgroup (16 waves): wave w takes query half
+// w & 1 of tile (w >> 1) & 1 and the key tiles of part w >> 2.  The four
+// waves of a part share its K chunks (each loads 8 of the 32 rows), so each
+// chunk in LDS serves 128 queries: half the K loads per query of the
+// one-tile form, and room in LDS for an NST-deep ring at 16 waves per CU
+// (the one-tile form runs two workgroups of 8 waves per CU with a 2-deep
+// ring: its waves wait on their next chunk).  Per query the arithmetic and
+// its order are those of cs4a_score_kernel: the scores are bit-identical.
+constexpr int kScore2Tiles = 2;
+constexpr int kScore2Threads = 2 * 64 * kScoreParts * kScore2Tiles;
+
+template <int D, int NST>
+__global__ __launch_bounds__(kScore2Threads) void cs4a_score2_kernel(const ScoreArgs a) {
+    constexpr int KSTEPS = D / 16;
+    constexpr int ROWB = D * 2;
+    constexpr int CH = D / 8;
+    constexpr int STAGE = 32 * ROWB;
+    constexpr int RPL = 1024 / ROWB;
+    constexpr int LOADS = 8 / RPL;                                 // load instructions per wave per chunk
+    constexpr int NQ = 64 * kScore2Tiles;                          // queries per workgroup
+    constexpr float kLazy = 8.0f;
+    extern __shared__ __attribute__((aligned(1024))) char dyn[];
+    char* kst_base = dyn;                                          // [part][stage][STAGE]
+    const int tpp = a.nkb / 2 + 2;
+    ScoreChunk* table = (ScoreChunk*)(dyn + kScoreParts * NST * STAGE);   // [part][tpp]
+    int* halves = (int*)(table + kScoreParts * tpp);                         // [nkb]
+    int* nchunks = halves + a.nkb;                                 // [part]
+    float* mrow = (float*)(nchunks + kScoreParts);                 // [part][NQ]
+    float* lrow = mrow + NQ * kScoreParts;                         // [part][NQ]
+    float* acc = lrow + NQ * kScoreParts;                          // [nkb][NQ]
+
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int qh = wave & 1, tq = (wave >> 1) & 1, par = wave >> 2;
+    const int wip = wave & 3;                                      // wave within its part
+    const int n = lane & 31, g = lane >> 5;
+    const int q = tq * 64 + qh * 32 + n;                           // query within the workgroup
+    const int ntp = (a.nqb + 1) >> 1;
+    const int bh = blockIdx.x / ntp, tp = blockIdx.x - bh * ntp;
+    const int qt = 2 * tp + tq;
+    const bool tile_ok = qt < a.nqb;                               // an odd last tile pairs with nothing
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int nkb = a.nkb;
+
+    const int nbq = a.d_side >> 3;
+    const int qtc = tile_ok ? qt : a.nqb - 1;
+    const int ti = qtc / nbq, tj = qtc - ti * nbq;
+    const int64_t tok = (int64_t)(8 * ti + 4 * qh + (n >> 3)) * a.d_side + 8 * tj + (n & 7);
+    const __bf16* qp = a.q + b * a.sq_b + h * a.sq_h + tok * a.sq_t;
+    bf16x8 qreg[KSTEPS];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qreg[s] = *(const bf16x8*)(qp + 16 * s + 8 * g);
+    const __bf16* kh = a.k + b * a.sk_b + h * a.sk_h;
+
+    // chunk table: one thread per key tile
+    int my_tile_rows = 0, my_s = 0, my_ta = 0, my_tb = 0;
+    if (tid < nkb) {
+        my_s = scale_of_tile(a.g, tid);
+        const int local = tid - a.g.tile_base[my_s];
+        my_ta = local / a.g.nb[my_s];
+        my_tb = local - my_ta * a.g.nb[my_s];
+        my_tile_rows = min(8, a.g.side[my_s] - 8 * my_ta);
+        halves[tid] = my_tile_rows > 4 ? 2 : 1;
+    }
+    if (tid < kScoreParts) nchunks[tid] = 0;
+    for (int i = tid; i < nkb * NQ; i += kScore2Threads) acc[i] = 0.0f;
+    __syncthreads();
+    if (tid < nkb) {
+        const int p = tid % kScoreParts;
+        int off = 0;
+        for (int j = p; j < tid; j += kScoreParts) off += halves[j];
+        const int side = a.g.side[my_s];
+        const int cols = min(8, side - 8 * my_tb);
+        for (int hh = 0; hh < halves[tid]; ++hh) {
+            ScoreChunk c;
+            c.base = a.g.tok_off[my_s] + (8 * my_ta + 4 * hh) * side + 8 * my_tb;
+            c.stride = side;
+            c.tile = tid;
+            c.shape = min(4, my_tile_rows - 4 * hh) | (cols << 4);
+            table[p * tpp + off + hh] = c;
+        }
+        if (tid + kScoreParts >= nkb) nchunks[p] = off + halves[tid];
+    }
+    __syncthreads();
+    const int nch = nchunks[par];
+    int nmax = 0;
+#pragma unroll
+    for (int p = 0; p < kScoreParts; ++p) nmax = max(nmax, nchunks[p]);
+    const ScoreChunk* mytab = table + par * tpp;
+    wait_vmcnt(0);   // Q is in registers before LDS-DMA traffic starts
+
+    const uint32_t kst0 = lds_addr(kst_base) + (uint32_t)(par * NST * STAGE);
+    auto issue = [&](int ci) {
+        const ScoreChunk c = mytab[ci];
+        const int nrows = c.shape & 15, ncols = c.shape >> 4;
+        const uint32_t kst = kst0 + (uint32_t)((ci % NST) * STAGE);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int row = 8 * wip + i * RPL + lane / CH;
+            const int lc = (lane % CH) ^ swz<CH>(row);
+            const int r = row >> 3, col = row & 7;
+            const bool valid = r < nrows && col < ncols;
+            const int t = valid ? c.base + r * c.stride + col : c.base;
+            lds_dma16(kh + t * a.sk_t + lc * 8,
+                      __builtin_amdgcn_readfirstlane(kst + (uint32_t)((8 * wip + i * RPL) * ROWB)));
+        }
+    };
+
+    const float cl = a.scale_log2;
+    float m_run = -INFINITY;
+    for (int k = 0; k < NST - 1 && k < nch; ++k) issue(k);
+    for (int ci = 0; ci < nmax; ++ci) {
+        const int ahead = min(NST - 2, nch - 1 - ci);             // chunks issued after chunk ci
+        if (ahead >= 2) wait_vmcnt(2 * LOADS);
+        else if (ahead == 1) wait_vmcnt(LOADS);
+        else wait_vmcnt(0);
+        wg_barrier();
+        if (ci + NST - 1 < nch) issue(ci + NST - 1);
+        if (ci < nch) {
+            const ScoreChunk c = mytab[ci];
+            const int cr = c.shape & 15, ccn = c.shape >> 4, ct = c.tile;
+            const char* kst = kst_base + (par * NST + ci % NST) * STAGE;
+            f32x16 sacc = (f32x16)0.0f;
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                const int pc = (2 * s + g) ^ swz<CH>(n);
+                const bf16x8 kop = *(const bf16x8*)(kst + n * ROWB + pc * 16);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[s], sacc, 0, 0, 0);
+            }
+            if (cr < 4 || ccn < 8) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = i >> 2, col = 4 * g + (i & 3);
+                    if (!(r < cr && col < ccn)) sacc[i] = -INFINITY;
+                }
+            }
+            float mx = sacc[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            const float cand = mx * cl;
+            const bool need = cand > m_run + kLazy;
+            if (__ballot(need)) {
+                if (need) {
+                    const float alpha = __builtin_amdgcn_exp2f(m_run - cand);
+                    if (g == 0)
+                        for (int kt = par; kt <= ct; kt += kScoreParts) acc[kt * NQ + q] *= alpha;
+                    m_run = cand;
+                }
+            }
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) part += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], cl, -m_run));
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+            part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            if (g == 0) acc[ct * NQ + q] += part;
+        }
+    }
+
+    // merge the parts: common max M, total l, then normalise
+    float l_mine = 0.0f;
+    if (g == 0)
+        for (int kt = par; kt < nkb; kt += kScoreParts) l_mine += acc[kt * NQ + q];
+    if (g == 0) {
+        mrow[par * NQ + q] = m_run;
+        lrow[par * NQ + q] = l_mine;
+    }
+    __syncthreads();
+    if (g == 0) {
+        float M = mrow[q];
+#pragma unroll
+        for (int p = 1; p < kScoreParts; ++p) M = fmaxf(M, mrow[p * NQ + q]);
+        float l_q = 0.0f;
+#pragma unroll
+        for (int p = 0; p < kScoreParts; ++p) {
+            const float mp = mrow[p * NQ + q];
+            if (mp != -INFINITY) l_q += lrow[p * NQ + q] * __builtin_amdgcn_exp2f(mp - M);
+        }
+        const float f = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M) / l_q;
+        for (int kt = par; kt < nkb; kt += kScoreParts) acc[kt * NQ + q] *= f;
+    }
+    __syncthreads();
+    for (int e = tid; e < kScore2Tiles * nkb; e += kScore2Threads) {
+        const int t2 = e / nkb, kt = e - t2 * nkb;
+        if (2 * tp + t2 >= a.nqb) continue;
+        float sum = 0.0f;
+        for (int qq = 0; qq < 64; ++qq) sum += acc[kt * NQ + t2 * 64 + qq];
+        a.scores[((int64_t)bh * a.nqb + 2 * tp + t2) * nkb + kt] = sum * (1.0f / 64.0f);
+    }
+}
+
 __device__ __forceinline__ int64_t quantise(float s) {
     const float x = s * 16777216.0f;   // exact: power-of-two scaling
     return x >= 0.0f ? (int64_t)floorf(x) : 0;
@@ -370,23 +563,43 @@ __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a
     if (lane == 0) a.kv_cnt[tg][(int64_t)bh * nqbT + qt] = base;
 }
 
-hipError_t launch_cs4a_score(const ScoreArgs& a, int head_dim, hipStream_t stream) {
-    const size_t shmem = (size_t)kScoreParts * kScoreStages * 32 * head_dim * 2 +
-                         kScoreParts * (size_t)(a.nkb / 2 + 2) * sizeof(ScoreChunk) + (size_t)(a.nkb + kScoreParts) * sizeof(int) +
-                         2 * 64 * kScoreParts * sizeof(float) + (size_t)a.nkb * 64 * sizeof(float);
-    dim3 grid((unsigned)(a.nqb * a.B * a.H)), block(kScoreThreads);
-    if (head_dim == 128) {
-        hipError_t e = hipFuncSetAttribute((const void*)cs4a_score_kernel<128>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(cs4a_score_kernel<128>, grid, block, shmem, stream, a);
-    } else {
-        hipError_t e = hipFuncSetAttribute((const void*)cs4a_score_kernel<64>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(cs4a_score_kernel<64>, grid, block, shmem, stream, a);
-    }
+namespace {
+
+size_t score_shmem(int parts, int stages, int head_dim, int nkb, int nq) {
+    return (size_t)parts * stages * 32 * head_dim * 2 + parts * (size_t)(nkb / 2 + 2) * sizeof(ScoreChunk) +
+           (size_t)(nkb + parts) * sizeof(int) + 2 * (size_t)nq * parts * sizeof(float) +
+           (size_t)nkb * nq * sizeof(float);
+}
+
+template <typename K>
+hipError_t launch_with_shmem(K kernel, dim3 grid, dim3 block, size_t shmem, const ScoreArgs& a, hipStream_t stream) {
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, a);
     return hipGetLastError();
+}
+
+constexpr size_t kLdsBytes = 160 * 1024;
+
+}  // namespace
+
+hipError_t launch_cs4a_score(const ScoreArgs& a, int head_dim, hipStream_t stream) {
+    // two query tiles per workgroup with the deepest ring that fits one CU's LDS;
+    // else (many key tiles) one tile per workgroup
+    const dim3 grid2((unsigned)(((a.nqb + 1) / 2) * a.B * a.H)), block2(kScore2Threads);
+    const size_t s4 = score_shmem(kScoreParts, 4, head_dim, a.nkb, 128);
+    const size_t s3 = score_shmem(kScoreParts, 3, head_dim, a.nkb, 128);
+    if (head_dim == 128) {
+        if (s4 <= kLdsBytes) return launch_with_shmem(cs4a_score2_kernel<128, 4>, grid2, block2, s4, a, stream);
+        if (s3 <= kLdsBytes) return launch_with_shmem(cs4a_score2_kernel<128, 3>, grid2, block2, s3, a, stream);
+    } else {
+        if (s4 <= kLdsBytes) return launch_with_shmem(cs4a_score2_kernel<64, 4>, grid2, block2, s4, a, stream);
+        if (s3 <= kLdsBytes) return launch_with_shmem(cs4a_score2_kernel<64, 3>, grid2, block2, s3, a, stream);
+    }
+    const size_t shmem = score_shmem(kScoreParts, kScoreStages, head_dim, a.nkb, 64);
+    const dim3 grid((unsigned)(a.nqb * a.B * a.H)), block(kScoreThreads);
+    if (head_dim == 128) return launch_with_shmem(cs4a_score_kernel<128>, grid, block, shmem, a, stream);
+    return launch_with_shmem(cs4a_score_kernel<64>, grid, block, shmem, a, stream);
 }
 
 hipError_t launch_cs4a_select_map(const SelMapArgs& a, int bh, hipStream_t stream) {

@@ -218,3 +218,25 @@ def test_multi_target_map_computes_scores():
     torch.cuda.synchronize()
     assert torch.equal(s1, s2)
     assert torch.equal(multi[-1][0], kc) and torch.equal(multi[-1][1], ki)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_scores_odd_tile_count_fallback_and_head_dims(d):
+    """Decision scale side 40 (25 query tiles: the scoring workgroups take
+    query tiles two at a time, so the last one holds a single tile) and side
+    64 of the 16-scale schedule (172 key tiles: too many for the two-tile
+    workgroup's accumulator in LDS, so one tile per workgroup), head dims 128
+    and 64: scores within tolerance of the oracle, rows summing to 1."""
+    vs = _vs()
+    for w, D, T, H in ((W.CS4A, 10, 11, 3), (W.HIGH_RES, 12, 15, 1)):
+        print(f"scores: side {w.sides[D]} d={d}", flush=True)
+        q_d, k, _ = spatial(w, B=1, H=H, q_side=w.sides[D])
+        if d != w.d:
+            q_d, k = q_d[..., :d].copy(), k[..., :d].copy()
+        scores, _, _, _, _ = vs.map_indices(w.sides, w.tile, D, T, w.n_sink, W.CS4A_TOP_P, q_d=to_device(q_d),
+                                            k=to_device(k))
+        torch.cuda.synchronize()
+        s = scores.cpu().numpy()
+        ref = OC.block_scores(q_d, k, w.sides, D, w.tile, 1 / math.sqrt(d))
+        assert np.abs(s - ref).max() <= SCORE_TOL, (w.sides[D], d)
+        assert np.abs(s.astype(np.float64).sum(-1) - 1).max() < 1e-4
