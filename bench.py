@@ -31,9 +31,11 @@ PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per launch of the sparse attention kernel on this workload, from
 # rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by a 256 MiB copy
-# (x2.000 and x1.000), recorded with the SHA-256 of the kernel sources they
-# were taken on; reported only while those sources are unchanged.
-TRAFFIC = {"bytes": 424.9e6, "sources_sha256": "35afcec37982cb5f32788cef54f760dee33f92adf69f97d8340f7997ba60849c"}
+# (x2.000 and x1.000), and its MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES
+# over GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), recorded with the SHA-256 of the
+# kernel sources they were taken on; reported only while those sources are
+# unchanged.
+TRAFFIC = {"bytes": 424.9e6, "mfma_busy": 0.352, "sources_sha256": "35afcec37982cb5f32788cef54f760dee33f92adf69f97d8340f7997ba60849c"}
 KERNEL_SOURCES = ("block_sparse_cross_csla_amd/csrc/attn_bf16.hip", "block_sparse_cross_csla_amd/csrc/common.h",
                   "block_sparse_cross_csla_amd/csrc/kernel_args.h")
 
@@ -265,6 +267,8 @@ def main():
                      "traffic_unit": "bytes per launch",
                      "traffic_tb_per_s": (TRAFFIC["bytes"] / (attn_ms * 1e-3) / 1e12
                                           if kernel_sources_sha256() == TRAFFIC["sources_sha256"] else None),
+                     "mfma_busy": (TRAFFIC["mfma_busy"]
+                                   if kernel_sources_sha256() == TRAFFIC["sources_sha256"] else None),
                      "kernel": "attn_fwd_bf16_kernel<128,false,false>",
                      "flop_per_launch": flops},
     }
