@@ -308,3 +308,32 @@ def test_odd_head_count_every_tile_all_list_kernels():
     torch.cuda.synchronize()
     ro, rl = OA.token_masked_attention(q64, k64, v64, sides, qs, t, n_sink, rad, scale)
     _compare(o, lse, ro, rl, BF16_TOL, "odd heads token-exact")
+
+
+def test_more_than_64_tiles_per_head_every_tile():
+    """Query side 96 (144 query tiles, 72 pairs: more than the 64 items per
+    head the dispatch order ranks, so these heads keep the natural order),
+    B=1, H=3, per-head random lists of varied lengths with an empty and a
+    full row: every query tile of every head against the oracle for the
+    64-query and the paired-tile kernels."""
+    vs = _vs()
+    sides, qs, t = (1, 2, 4, 8, 16, 32, 48, 64, 96), 8, 8
+    B, H, d = 1, 3, 128
+    scale = 1 / math.sqrt(d)
+    nqb, nkb, nq, nk = G.counts(sides, qs, t)
+    assert nqb == 144
+    rng = np.random.default_rng(97)
+    keep = rng.random((B, H, nqb, nkb)) < rng.choice([0.02, 0.08, 0.2], size=(B, H, nqb, 1))
+    keep[0, 1, 5] = False
+    keep[0, 2, 100] = True
+    cnt, idx = lists(keep)
+    q, k, v = gaussian(9, 91, B, H, nq, nk, d)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    ro, rl = OA.block_sparse_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                       sides, qs, t, cnt, idx, scale)
+    cd, idd = torch.from_numpy(cnt).cuda(), torch.from_numpy(idx).cuda()
+    for name, fn in (("64-query", vs.attn_fwd), ("paired", vs.attn_fwd_pair)):
+        print(f"144 tiles: {name}", flush=True)
+        o, lse = fn(qd, kd, vd, sides, t, qs, cd, idd)
+        torch.cuda.synchronize()
+        _compare(o, lse, ro, rl, BF16_TOL, f"144 tiles {name}")
