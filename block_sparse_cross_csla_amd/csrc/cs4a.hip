@@ -430,7 +430,7 @@ __device__ __forceinline__ int64_t quantise(float s) {
 // reads), keeps the selection as a bitset in registers (one ballot per 64
 // tiles), then decides every target key tile and compacts the list with
 // ballots, one key scale at a time: each decision row block's footprint on
-// the key scale is computed once per wave (exact double quotients), and a
+// the key scale is computed once per wave (exact integer quotients), and a
 // key tile is kept iff a selected decision tile's row and column footprints
 // both meet it.  The wave whose target tile is the first child of its parent
 // also writes the parent's selection (sel_cnt / sel_idx) when asked to.
@@ -508,6 +508,11 @@ __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a
     __shared__ uint32_t srows[4][16];
     __shared__ int2 fp[4][16];
     const int tbD = a.g.tile_base[D];
+    // the geometry of scale `lane` in that lane (read with readlane below, not
+    // through a chain of dependent scalar loads per scale)
+    const int g_tb = lane <= a.g.n_scales ? a.g.tile_base[min(lane, kMaxScales)] : 0;
+    const int g_side = lane < a.g.n_scales ? a.g.side[min(lane, kMaxScales - 1)] : 0;
+    const int g_nb = lane < a.g.n_scales ? a.g.nb[min(lane, kMaxScales - 1)] : 1;
     if (lane < nbD) {
         uint32_t r = 0;
         for (int sb = 0; sb < nbD; ++sb) r |= (uint32_t)selected(tbD + lane * nbD + sb) << sb;
@@ -517,13 +522,14 @@ __global__ __launch_bounds__(256) void cs4a_select_map_kernel(const SelMapArgs a
     int base = 0;
     int32_t* out = a.kv_idx[tg] + ((int64_t)bh * nqbT + qt) * nkbT;
     for (int s = 0; s <= T; ++s) {
-        const int tb0 = a.g.tile_base[s], tb1 = a.g.tile_base[s + 1];
-        const int hs = a.g.side[s], nbs = a.g.nb[s];
+        const int tb0 = __builtin_amdgcn_readlane(g_tb, s), tb1 = __builtin_amdgcn_readlane(g_tb, s + 1);
+        const int hs = __builtin_amdgcn_readlane(g_side, s), nbs = __builtin_amdgcn_readlane(g_nb, s);
         if (s >= D) {
             if (lane < nbD) {
+                // floor / ceil of exact quotients: sides are below 2^15, products below 2^30
                 const int ey = min(lane * t + t, hD);
-                const int lo = (int)floor((double)((int64_t)lane * t * hs) / (double)hD);
-                const int hi = (int)ceil((double)((int64_t)ey * hs) / (double)hD) - 1;
+                const int lo = (int)((uint32_t)(lane * t) * (uint32_t)hs / (uint32_t)hD);
+                const int hi = (int)(((uint32_t)ey * (uint32_t)hs + (uint32_t)hD - 1u) / (uint32_t)hD) - 1;
                 fp[wave][lane] = make_int2(lo, hi);
             }
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
