@@ -31,11 +31,52 @@ __device__ __forceinline__ int row_gap(int qi, int ka, int t, int h, int H) {
     return max(0, max(klo - hi, lo - khi));
 }
 
-__device__ __forceinline__ int tile_gap(const DevGeom& g, int s, int local, int ti, int tj, int H) {
-    const int nb = g.nb[s], t = g.tile, h = g.side[s];
+__device__ __forceinline__ int tile_gap(int nb, int t, int h, int local, int ti, int tj, int H) {
     const int a = local / nb, b = local - a * nb;
     return max(row_gap(ti, a, t, h, H), row_gap(tj, b, t, h, H));
 }
+
+// The geometry of scale `lane` held in that lane (every wave alike), so that
+// a thread finds the scale of its key tile, and that scale's numbers, with a
+// uniform loop of lane reads (readlane ignores the execution mask, so this
+// also holds in divergent code), not with a chain of dependent loads from the
+// kernel arguments.
+struct ScaleOf {
+    int s, tb, nb, side, radius;
+};
+
+struct LaneScales {
+    int tb, nb, side, radius;   // tile_base / nb / side / radius of scale `lane`
+    int n;                      // number of scales
+
+    __device__ static LaneScales load(const MaskArgs& a, int lane) {
+        LaneScales r;
+        r.n = a.g.n_scales;
+        const bool in = lane < r.n;
+        const int s = min(lane, kMaxScales - 1);
+        r.tb = in ? a.g.tile_base[s] : 0;
+        r.nb = in ? a.g.nb[s] : 1;
+        r.side = in ? a.g.side[s] : 1;
+        r.radius = in ? a.radius[s] : -1;
+        return r;
+    }
+    // key tile `id` lies in the last scale that starts at or before it
+    __device__ ScaleOf find(int id) const {
+        ScaleOf r{0, __builtin_amdgcn_readlane(tb, 0), __builtin_amdgcn_readlane(nb, 0),
+                  __builtin_amdgcn_readlane(side, 0), __builtin_amdgcn_readlane(radius, 0)};
+        for (int u = 1; u < n; ++u) {
+            const int b = __builtin_amdgcn_readlane(tb, u);
+            if (id >= b) {
+                r.s = u;
+                r.tb = b;
+                r.nb = __builtin_amdgcn_readlane(nb, u);
+                r.side = __builtin_amdgcn_readlane(side, u);
+                r.radius = __builtin_amdgcn_readlane(radius, u);
+            }
+        }
+        return r;
+    }
+};
 
 __global__ __launch_bounds__(256) void csla_mask_kernel(const MaskArgs a) {
     extern __shared__ uint64_t rank_key[];   // budget mode: one packed key per tile
@@ -46,11 +87,14 @@ __global__ __launch_bounds__(256) void csla_mask_kernel(const MaskArgs a) {
     const int ti = qt / nbq, tj = qt - ti * nbq;
     const int nkb = a.nkb;
     const bool budget = a.budget > 0;
+    const LaneScales ls = LaneScales::load(a, lane);
+    auto gap = [&](int j, const ScaleOf& f) { return tile_gap(f.nb, a.g.tile, f.side, j - f.tb, ti, tj, H); };
 
     if (budget) {
         for (int j = tid; j < nkb; j += 256) {
-            const int s = scale_of_tile(a.g, j);
-            const uint64_t dist = (uint64_t)tile_gap(a.g, s, j - a.g.tile_base[s], ti, tj, H);
+            const ScaleOf f = ls.find(j);
+            const int s = f.s;
+            const uint64_t dist = (uint64_t)gap(j, f);
             rank_key[j] = ((uint64_t)(s >= a.n_sink) << 62) | (dist << 30) |
                           ((uint64_t)(31 - s) << 25) | (uint64_t)j;
         }
@@ -68,9 +112,8 @@ __global__ __launch_bounds__(256) void csla_mask_kernel(const MaskArgs a) {
                 for (int i = 0; i < nkb; ++i) rank += rank_key[i] < mine;
                 keep = rank < a.keep_n;
             } else {
-                const int s = scale_of_tile(a.g, j);
-                keep = s < a.n_sink ||
-                       (a.radius[s] >= 0 && tile_gap(a.g, s, j - a.g.tile_base[s], ti, tj, H) <= a.radius[s]);
+                const ScaleOf f = ls.find(j);
+                keep = f.s < a.n_sink || (f.radius >= 0 && gap(j, f) <= f.radius);
             }
             if (a.mask != nullptr) a.mask[(int64_t)qt * nkb + j] = keep ? 1 : 0;
         }
