@@ -88,3 +88,30 @@ def test_map_indices_checks():
     bad = (torch.zeros(1, 2, nqbT, dtype=torch.int32), torch.zeros(1, 2, nqbT, nkbT - 1, dtype=torch.int32))
     with pytest.raises(ValueError, match="per-head lists"):
         vs.map_indices(SIDES, T, D, TT, 5, 0.9, scores=torch.zeros(1, 2, nqbD, nkbD), out=bad)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built library the package refuses to import: there is no
+    fallback path that could compute without the HIP kernels."""
+    import os
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.dirname(os.path.abspath(vs.__file__))
+    shutil.copytree(src, tmp_path / "block_sparse_cross_csla_amd", ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    r = subprocess.run([sys.executable, "-c", "import block_sparse_cross_csla_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libvarsparse.so is missing" in r.stderr
+
+
+def test_product_sources_never_reach_the_oracle():
+    """The package (binding and kernels) neither imports nor names the CPU
+    oracle, which is test infrastructure only."""
+    import os
+    root = os.path.dirname(os.path.abspath(vs.__file__))
+    for dirpath, _, files in os.walk(root):
+        for name in files:
+            if name.endswith((".py", ".hip", ".h", ".cpp")):
+                with open(os.path.join(dirpath, name), encoding="utf-8") as fh:
+                    assert "oracle" not in fh.read(), os.path.join(dirpath, name)
