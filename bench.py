@@ -94,7 +94,7 @@ def kept_flops(cnt, idx, sizes, q_tile_tokens, d, heads):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py runs on one GPU: the kernels use one device; --gpus must be 1"}))
         sys.exit(2)
     import torch
     import block_sparse_cross_csla_amd as vs
