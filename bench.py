@@ -59,6 +59,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cs4a", action="store_true")
+    p.add_argument("--no-high-res", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-single", action="store_true",
                    help="skip the single-launch warm/cold timings (keeps counter runs to back-to-back launches)")
@@ -290,6 +291,10 @@ def main():
         result["scale_loop"] = bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev)
         print("[bench] scale loop done", file=sys.stderr, flush=True)
 
+    if not args.no_high_res:
+        result["high_res"] = bench_high_res(vs, torch, W, SpatialField, to_dev, args, stream, dev)
+        print("[bench] high-res done", file=sys.stderr, flush=True)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q_np, k_np, v_np, cnt_h, idx_h, sizes, round_bf16, args.cpu_seconds)
         print("[bench] cpu baseline done", file=sys.stderr, flush=True)
@@ -400,6 +405,64 @@ def bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev):
                        "correct_side64_bytes": corr_bytes,
                        "correct_side64_gbps": corr_bytes / (res["correct_last"] * 1e-3) / 1e9,
                        "hbm_peak_gbps": 8000.0}}
+
+
+def bench_high_res(vs, torch, W, SpatialField, to_dev, args, stream, dev):
+    """The side-128 query scale over the 16-scale cache (42521 tokens), B = 1,
+    H = 16, CSLA radius 2: mask + block-sparse attention steps, the attention
+    alone, and the dense kernel on the same tensors."""
+    w = W.HIGH_RES
+    f = SpatialField(w.seed, w.wid, w.B, w.H, w.d)
+    k_np, v_np = f.keys_values(w.sides[: w.q_scale + 1], w.n_sink, largest_side=w.sides[w.q_scale])
+    q, k, v = to_dev(f.queries(w.sides[w.q_scale])), to_dev(k_np), to_dev(v_np)
+    del k_np, v_np
+    nqb, nkb, nq, nk = vs.geom_counts(w.sides, w.tile, w.q_scale)
+    cnt = torch.empty(nqb, dtype=torch.int32, device=dev)
+    idx = torch.empty(nqb, nkb, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(w.d)
+
+    def mask():
+        vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, radius=w.radii, out=(cnt, idx, None), stream=stream)
+
+    def attn():
+        vs.attn_fwd(q, k, v, w.sides, w.tile, w.q_scale, cnt, idx, softmax_scale=scale, out=o, want_lse=False,
+                    stream=stream)
+
+    def step():
+        mask()
+        attn()
+
+    def run(fn, warm, reps):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    reps = max(5, args.steps // 4)
+    step_ms = run(step, 50, reps)
+    attn_ms = run(attn, 2, reps)
+    dense_ms = run(lambda: vs.dense_attn_fwd(q, k, v, softmax_scale=scale, out=o, want_lse=False, stream=stream),
+                   2, max(3, args.steps // 40))
+    mask()
+    torch.cuda.synchronize()
+    cnt_h, idx_h = cnt.cpu().numpy(), idx.cpu().numpy()
+    sizes = tile_sizes(w.sides, w.q_scale, w.tile)
+    flops = kept_flops(cnt_h, idx_h, sizes, w.tile * w.tile, w.d, w.B * w.H)
+    dense_flops = 4.0 * w.d * nq * nk * w.B * w.H
+    return {"workload": "high_res_128", "B": w.B, "H": w.H, "head_dim": w.d, "query_side": w.sides[w.q_scale],
+            "cached_tokens": nk, "radius": w.radius, "ms_per_step": step_ms, "attn_kernel_ms": attn_ms,
+            "dense_kernel_ms": dense_ms, "effective_tflops": flops / (step_ms * 1e-3) / 1e12,
+            "attn_tflops": flops / (attn_ms * 1e-3) / 1e12, "speedup_vs_dense": dense_ms / step_ms,
+            "kernel_speedup_vs_dense": dense_ms / attn_ms,
+            "count_sparsity": float(1.0 - cnt_h.sum() / (nqb * nkb)), "flop_sparsity": float(1.0 - flops / dense_flops),
+            "timed": "mask + attention steps; the attention alone; the dense kernel, HIP events around back-to-back runs"}
 
 
 def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
