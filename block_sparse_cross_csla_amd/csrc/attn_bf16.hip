@@ -23,9 +23,10 @@
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in
 //    registers for the whole walk), so that every lane holds the scores of a
 //    single query: the row max needs one v_permlane32_swap, row sums none;
-//  * online softmax in the exp2 domain; the running max is only raised when a
-//    new score exceeds it by more than 2^8 in the exponent (exact in
-//    arithmetic: the final normalisation uses the same stale max);
+//  * online softmax in the exp2 domain against the running maximum: the
+//    chunk's own maximum is taken only on a rare path, when a weight would
+//    exceed 2^16 (exact in arithmetic: the final normalisation uses the same
+//    running maximum);
 //  * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T
 //    accumulator registers (no data movement), V^T is read from LDS with
 //    gfx950's transposing ds_read_b64_tr_b16.
@@ -186,7 +187,7 @@ __device__ __forceinline__ void make_plan(LoadPlan<D>& p, int wave, int lane, in
 
 template <int D>
 __device__ __forceinline__ void load_chunk(const LoadPlan<D>& p, const __bf16* kh, const __bf16* vh, int32_t krb,
-                                           int32_t vrb, const Chunk& c, uint32_t k_lds, uint32_t v_lds,
+                                           int32_t vrb, const Chunk& c, lds_ptr k_lds, lds_ptr v_lds,
                                            int wave, int lane) {
     using P = LoadPlan<D>;
     if (c.full) {
@@ -194,9 +195,9 @@ __device__ __forceinline__ void load_chunk(const LoadPlan<D>& p, const __bf16* k
         for (int i = 0; i < P::LOADS; ++i) {
             const int r = (16 * wave + i * P::RPL) >> 3;     // chunk row of this load (wave-uniform)
             const int32_t t0 = c.base + r * c.stride;
-            const uint32_t dst = (uint32_t)((16 * wave + i * P::RPL) * P::ROWB);
-            lds_dma16_off(kh, t0 * krb + p.kc[i], __builtin_amdgcn_readfirstlane(k_lds + dst));
-            lds_dma16_off(vh, t0 * vrb + p.vc[i], __builtin_amdgcn_readfirstlane(v_lds + dst));
+            const int dst = (16 * wave + i * P::RPL) * P::ROWB;
+            dma16(kh, (uint32_t)(t0 * krb + p.kc[i]), k_lds + dst);
+            dma16(vh, (uint32_t)(t0 * vrb + p.vc[i]), v_lds + dst);
         }
     } else {
 #pragma unroll
@@ -207,9 +208,9 @@ __device__ __forceinline__ void load_chunk(const LoadPlan<D>& p, const __bf16* k
             // padding slots re-read the chunk's first token (finite values; masked later)
             const bool valid = r < c.nrows && col < c.ncols && slot < c.nvalid;
             const int32_t tok = valid ? c.base + r * c.stride + col : c.base;
-            const uint32_t dst = (uint32_t)((16 * wave + i * P::RPL) * P::ROWB);
-            lds_dma16_off(kh, tok * krb + unit16, __builtin_amdgcn_readfirstlane(k_lds + dst));
-            lds_dma16_off(vh, tok * vrb + unit16, __builtin_amdgcn_readfirstlane(v_lds + dst));
+            const int dst = (16 * wave + i * P::RPL) * P::ROWB;
+            dma16(kh, (uint32_t)(tok * krb + unit16), k_lds + dst);
+            dma16(vh, (uint32_t)(tok * vrb + unit16), v_lds + dst);
         }
     }
 }
@@ -232,6 +233,24 @@ __device__ __forceinline__ float half_swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Weights of the fast softmax path stay at or below this (log2 domain: at most
+// 16 above the running maximum), far inside the range of bf16 and float.
+constexpr float kSumCap = 65536.0f;
+
+// P^T = exp2(S^T c - m) rounded to bf16 (the PV operand), and the lane's sum
+// of the float weights (pairwise).
+__device__ __forceinline__ float exp_chunk(const f32x16& s, float c, float m, bf16x8 (&pt)[2]) {
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pt[i >> 3][i & 7] = (__bf16)p[i];
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = p[2 * i] + p[2 * i + 1];
+    return ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+}
+
 // Consume one chunk of 32 keys from LDS (kst: K rows, vst: V rows).  The
 // LDS operand reads of each phase are issued ahead of the MFMAs that consume
 // them (all K rows before S^T, all V^T reads before the softmax, so they land
@@ -245,7 +264,6 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
     constexpr int MBLK = D / 32;
     constexpr int ROWB = D * 2;
     constexpr int CH = D / 8;
-    constexpr float kLazy = 8.0f;
     const int n = lane & 31, g = lane >> 5;
 
     // S^T (32 keys x 32 queries) = K Q^T
@@ -298,28 +316,29 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
             if (!(r < cc.nrows && col < cc.ncols && key < cc.nvalid)) sacc[i] = -INFINITY;
         }
     }
-    // online softmax (log2 domain), running max raised lazily
-    float mx = sacc[0];
+    // online softmax (log2 domain) against the running maximum, with no
+    // maximum taken over the chunk first: when the 16 weights of a lane sum
+    // above kSumCap (or to inf / NaN, as on the first chunk, whose running
+    // maximum is still -1e30) the chunk is redone on a rare path that raises
+    // the running maximum to the chunk's and rescales O and the row sum.  Every
+    // weight of the fast path is below kSumCap, finite in bf16 and float, and
+    // the normalised result is the same softmax.
+    bf16x8 pt[2];
+    float sum = exp_chunk(sacc, c, st.m_run, pt);
+    if (__builtin_amdgcn_ballot_w64(!(sum <= kSumCap))) {
+        float mx = sacc[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
-    mx = half_swap_max(mx);
-    const float cand = mx * c;
-    const bool need = cand > st.m_run + kLazy;
-    if (__ballot(need)) {
-        const float m_new = need ? cand : st.m_run;
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+        mx = half_swap_max(mx);
+        const float m_new = fmaxf(st.m_run, mx * c);
         const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
 #pragma unroll
         for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] *= alpha;
         st.l_run *= alpha;
         st.m_run = m_new;
+        sum = exp_chunk(sacc, c, st.m_run, pt);
     }
-    bf16x8 pt[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c, -st.m_run));
-        st.l_run += p;
-        pt[i >> 3][i & 7] = (__bf16)p;
-    }
+    st.l_run += sum;
     __builtin_amdgcn_sched_barrier(0);
 
     // O^T (D x 32 queries) += V^T P^T
@@ -492,7 +511,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     const __bf16* vh = a.v + b * a.sv_b + h * a.sv_h;
     const int32_t krb = (int32_t)(a.sk_t * 2), vrb = (int32_t)(a.sv_t * 2);
     const float c = a.scale_log2;
-    const uint32_t lds0 = lds_addr(smem);
+    const lds_ptr L = (lds_ptr)smem;
     const char* sm = smem;
 
     // Q^T operands first: their loads are in flight while the walk is set up
@@ -547,7 +566,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         // the run's first chunk is known now: its loads overlap the table build
         if (w.cend > 0) {
             const int nv = min(32, w.cend);
-            load_chunk<D>(plan, kh, vh, krb, vrb, unpack_chunk(0, pack_info(8, 4, 8, nv)), lds0, lds0 + STAGE, wave,
+            load_chunk<D>(plan, kh, vh, krb, vrb, unpack_chunk(0, pack_info(8, 4, 8, nv)), L, L + STAGE, wave,
                           lane);
             first_loaded = true;
         }
@@ -594,14 +613,14 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         // loads of this chunk in LDS and has finished the previous chunk, whose
         // stage then takes the next prefetch
         Chunk cur = desc(0), nxt;
-        if (!first_loaded) load_chunk<D>(plan, kh, vh, krb, vrb, cur, lds0, lds0 + STAGE, wave, lane);
+        if (!first_loaded) load_chunk<D>(plan, kh, vh, krb, vrb, cur, L, L + STAGE, wave, lane);
         first_loaded = false;
         for (int ci = 0; ci < nch; ci += 2) {
             wait_vmcnt(0);
             wg_barrier();
             if (ci + 1 < nch) {
                 nxt = desc(ci + 1);
-                load_chunk<D>(plan, kh, vh, krb, vrb, nxt, lds0 + 2 * STAGE, lds0 + 3 * STAGE, wave, lane);
+                load_chunk<D>(plan, kh, vh, krb, vrb, nxt, L + 2 * STAGE, L + 3 * STAGE, wave, lane);
             }
             attend_chunk<D>(st, sm, sm + STAGE, cur, c, lane, TOKEN ? csla_token_bits(ts, cur, qy, qx, a.q_side, g) : 0xffffu);
             if (ci + 1 >= nch) break;
@@ -610,7 +629,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
             wg_barrier();
             if (ci + 2 < nch) {
                 nxt = desc(ci + 2);
-                load_chunk<D>(plan, kh, vh, krb, vrb, nxt, lds0, lds0 + STAGE, wave, lane);
+                load_chunk<D>(plan, kh, vh, krb, vrb, nxt, L, L + STAGE, wave, lane);
             }
             attend_chunk<D>(st, sm + 2 * STAGE, sm + 3 * STAGE, cur, c, lane,
                             TOKEN ? csla_token_bits(ts, cur, qy, qx, a.q_side, g) : 0xffffu);
@@ -695,16 +714,16 @@ __device__ __forceinline__ void make_pair_plan(PairPlan<D>& p, int wave, int lan
 // Wave `wave` fills key rows [8 wave, 8 wave + 8) of a stage: chunk row `wave`.
 template <int D>
 __device__ __forceinline__ void load_chunk_pair(const PairPlan<D>& p, const __bf16* kh, const __bf16* vh,
-                                                int32_t krb, int32_t vrb, const Chunk& c, uint32_t k_lds,
-                                                uint32_t v_lds, int wave, int lane) {
+                                                int32_t krb, int32_t vrb, const Chunk& c, lds_ptr k_lds,
+                                                lds_ptr v_lds, int wave, int lane) {
     using P = PairPlan<D>;
     if (c.full) {
         const int32_t t0 = c.base + wave * c.stride;
 #pragma unroll
         for (int i = 0; i < P::LOADS; ++i) {
-            const uint32_t dst = (uint32_t)((8 * wave + i * P::RPL) * P::ROWB);
-            lds_dma16_off(kh, t0 * krb + p.kc[i], __builtin_amdgcn_readfirstlane(k_lds + dst));
-            lds_dma16_off(vh, t0 * vrb + p.vc[i], __builtin_amdgcn_readfirstlane(v_lds + dst));
+            const int dst = (8 * wave + i * P::RPL) * P::ROWB;
+            dma16(kh, (uint32_t)(t0 * krb + p.kc[i]), k_lds + dst);
+            dma16(vh, (uint32_t)(t0 * vrb + p.vc[i]), v_lds + dst);
         }
     } else {
 #pragma unroll
@@ -714,9 +733,9 @@ __device__ __forceinline__ void load_chunk_pair(const PairPlan<D>& p, const __bf
             const int unit16 = ((lane % P::CH) ^ swz<P::CH>(slot)) * 16;
             const bool valid = r < c.nrows && col < c.ncols && slot < c.nvalid;
             const int32_t tok = valid ? c.base + r * c.stride + col : c.base;
-            const uint32_t dst = (uint32_t)((8 * wave + i * P::RPL) * P::ROWB);
-            lds_dma16_off(kh, tok * krb + unit16, __builtin_amdgcn_readfirstlane(k_lds + dst));
-            lds_dma16_off(vh, tok * vrb + unit16, __builtin_amdgcn_readfirstlane(v_lds + dst));
+            const int dst = (8 * wave + i * P::RPL) * P::ROWB;
+            dma16(kh, (uint32_t)(tok * krb + unit16), k_lds + dst);
+            dma16(vh, (uint32_t)(tok * vrb + unit16), v_lds + dst);
         }
     }
 }
@@ -822,7 +841,7 @@ __global__ __launch_bounds__(256, 2) void attn_pair_bf16_kernel(const AttnArgs a
     const __bf16* vh = a.v + b * a.sv_b + h * a.sv_h;
     const int32_t krb = (int32_t)(a.sk_t * 2), vrb = (int32_t)(a.sv_t * 2);
     const float c = a.scale_log2;
-    const uint32_t lds0 = lds_addr(smem);
+    const lds_ptr L = (lds_ptr)smem;
     const char* sm = smem;
 
     // ---- the two lists: membership bitmaps and the common leading run
@@ -907,8 +926,8 @@ __global__ __launch_bounds__(256, 2) void attn_pair_bf16_kernel(const AttnArgs a
         for (int k2 = 0; k2 < NST - 1; ++k2) {
             if (k2 < nch) {
                 ring[k2] = desc(k2, own[k2]);
-                load_chunk_pair<D>(plan, kh, vh, krb, vrb, ring[k2], lds0 + (uint32_t)(2 * k2 * STAGE),
-                                   lds0 + (uint32_t)((2 * k2 + 1) * STAGE), wave, lane);
+                load_chunk_pair<D>(plan, kh, vh, krb, vrb, ring[k2], L + 2 * k2 * STAGE, L + (2 * k2 + 1) * STAGE,
+                                   wave, lane);
             }
         }
         for (int ci0 = 0; ci0 < nch; ci0 += NST) {
@@ -926,8 +945,8 @@ __global__ __launch_bounds__(256, 2) void attn_pair_bf16_kernel(const AttnArgs a
                 const int nu = (u + NST - 1) % NST;                  // stage of chunk ci + NST - 1
                 if (ci + NST - 1 < nch) {
                     ring[nu] = desc(ci + NST - 1, own[nu]);
-                    load_chunk_pair<D>(plan, kh, vh, krb, vrb, ring[nu], lds0 + (uint32_t)(2 * nu * STAGE),
-                                       lds0 + (uint32_t)((2 * nu + 1) * STAGE), wave, lane);
+                    load_chunk_pair<D>(plan, kh, vh, krb, vrb, ring[nu], L + 2 * nu * STAGE,
+                                       L + (2 * nu + 1) * STAGE, wave, lane);
                 }
                 if (own[u] & mine) attend_chunk<D>(st, sm + 2 * u * STAGE, sm + (2 * u + 1) * STAGE, ring[u], c, lane);
             }

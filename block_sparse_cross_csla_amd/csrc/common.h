@@ -70,15 +70,6 @@ __device__ __forceinline__ int swz(int row) {
     return ((row & 3) << (CH == 16 ? 2 : 1)) | ((row >> 2) & (CH == 16 ? 3 : 1));
 }
 
-__device__ __forceinline__ void wait_vmcnt(int n) {
-    // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14];
-    // expcnt/lgkmcnt at their maximum = do not wait on them.
-    if (n == 2) __builtin_amdgcn_s_waitcnt(0x0F72);
-    else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
-    else if (n == 8) __builtin_amdgcn_s_waitcnt(0x0F78);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);   // anything else: wait for everything
-}
-
 // Workgroup barrier with no memory fence: the caller orders its own LDS-DMA
 // completions with wait_vmcnt; the asm memory clobber keeps the compiler from
 // moving LDS accesses across it.
@@ -86,21 +77,54 @@ __device__ __forceinline__ void wg_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
+typedef __attribute__((address_space(3))) char* lds_ptr;
+
 // 16 bytes per lane from global memory straight into LDS (gfx950
-// global_load_lds_dwordx4): lane i's bytes land at lds + 16 i.  Written as asm
-// so that the compiler neither reorders it across the explicit waits and
-// barriers of the pipeline nor inserts waits of its own for it; completion is
-// tracked by the caller with wait_vmcnt.  There is no destination register.
-__device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(gaddr), "s"(lds) : "memory", "m0");
+// global_load_lds_dwordx4): lane i's bytes land at dst + 16 i (dst wave
+// uniform).  The source is a wave-uniform 64-bit base (SGPR pair) plus a
+// per-lane 32-bit byte offset: one VALU add per load.  The LDS address goes to
+// the instruction through M0, passed as an input operand of the asm, so the
+// compiler writes M0 itself and knows it is read (nothing is clobbered); the
+// leading s_nop covers the M0-write-to-use hazard, which the compiler cannot
+// see inside the asm.  Written as asm so that the compiler does not treat it
+// as an LDS store: it would otherwise wait for every outstanding load before
+// each later LDS read.  Completion is ordered by the caller with wait_vm /
+// wait_all before the workgroup barrier that publishes the bytes.
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, lds_ptr dst) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)dst);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
 }
 
-// Same, addressed as a wave-uniform 64-bit base (SGPR pair) plus a per-lane
-// 32-bit byte offset: no 64-bit address arithmetic in VGPRs.
-__device__ __forceinline__ void lds_dma16_off(const void* base, int32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+// Same, from a per-lane 64-bit address.
+__device__ __forceinline__ void dma16_ptr(const void* gaddr, lds_ptr dst) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)dst);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "{m0}"(lds) : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (asm with a memory clobber, so that no load is moved across it).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    if (n == 2) wait_vm<2>();
+    else if (n == 4) wait_vm<4>();
+    else if (n == 8) wait_vm<8>();
+    else wait_vm<0>();   // anything else: wait for everything
+}
+
+// Wait until at most N vector-memory operations and no LDS operation of this
+// wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
+// Wait for every outstanding vector-memory and LDS operation of this wave.
+__device__ __forceinline__ void wait_all() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

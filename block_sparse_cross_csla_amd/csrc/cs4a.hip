@@ -124,11 +124,11 @@ __global__ __launch_bounds__(kScoreThreads) void cs4a_score_kernel(const ScoreAr
     const ScoreChunk* mytab = table + par * tpp;
     wait_vmcnt(0);   // Q is in registers before LDS-DMA traffic starts
 
-    const uint32_t kst0 = lds_addr(kst_base) + (uint32_t)(par * NST * STAGE);
+    const lds_ptr kst0 = (lds_ptr)kst_base + par * NST * STAGE;
     auto issue = [&](int ci) {
         const ScoreChunk c = mytab[ci];
         const int nrows = c.shape & 15, ncols = c.shape >> 4;
-        const uint32_t kst = kst0 + (uint32_t)((ci % NST) * STAGE);
+        const lds_ptr kst = kst0 + (ci % NST) * STAGE;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int row = 16 * qh + i * RPL + lane / CH;
@@ -136,8 +136,7 @@ __global__ __launch_bounds__(kScoreThreads) void cs4a_score_kernel(const ScoreAr
             const int r = row >> 3, col = row & 7;
             const bool valid = r < nrows && col < ncols;
             const int t = valid ? c.base + r * c.stride + col : c.base;
-            lds_dma16(kh + t * a.sk_t + lc * 8,
-                      __builtin_amdgcn_readfirstlane(kst + (uint32_t)((16 * qh + i * RPL) * ROWB)));
+            dma16_ptr(kh + t * a.sk_t + lc * 8, kst + (16 * qh + i * RPL) * ROWB);
         }
     };
 
@@ -316,11 +315,11 @@ __global__ __launch_bounds__(kScore2Threads) void cs4a_score2_kernel(const Score
     const ScoreChunk* mytab = table + par * tpp;
     wait_vmcnt(0);   // Q is in registers before LDS-DMA traffic starts
 
-    const uint32_t kst0 = lds_addr(kst_base) + (uint32_t)(par * NST * STAGE);
+    const lds_ptr kst0 = (lds_ptr)kst_base + par * NST * STAGE;
     auto issue = [&](int ci) {
         const ScoreChunk c = mytab[ci];
         const int nrows = c.shape & 15, ncols = c.shape >> 4;
-        const uint32_t kst = kst0 + (uint32_t)((ci % NST) * STAGE);
+        const lds_ptr kst = kst0 + (ci % NST) * STAGE;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int row = 8 * wip + i * RPL + lane / CH;
@@ -328,8 +327,7 @@ __global__ __launch_bounds__(kScore2Threads) void cs4a_score2_kernel(const Score
             const int r = row >> 3, col = row & 7;
             const bool valid = r < nrows && col < ncols;
             const int t = valid ? c.base + r * c.stride + col : c.base;
-            lds_dma16(kh + t * a.sk_t + lc * 8,
-                      __builtin_amdgcn_readfirstlane(kst + (uint32_t)((8 * wip + i * RPL) * ROWB)));
+            dma16_ptr(kh + t * a.sk_t + lc * 8, kst + (8 * wip + i * RPL) * ROWB);
         }
     };
 
