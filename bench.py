@@ -60,6 +60,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cs4a", action="store_true")
     p.add_argument("--no-high-res", action="store_true")
+    p.add_argument("--no-sweep", action="store_true", help="skip the 8B-shaped budget sweep")
+    # the GPU reaches steady clocks only after some hundreds of milliseconds of
+    # load: steps are run for this long before the --warmup count, whatever
+    # --warmup says, so that the timed steps and the per-kernel timings do not
+    # measure the clock ramp
+    p.add_argument("--settle-ms", type=float, default=400.0)
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-single", action="store_true",
                    help="skip the single-launch warm/cold timings (keeps counter runs to back-to-back launches)")
@@ -128,10 +134,19 @@ def main():
         vs.attn_fwd(q, k, v, w.sides, w.tile, w.q_scale, kv_cnt, kv_idx, softmax_scale=scale, out=o, lse=lse,
                     stream=stream)
 
+    # clock settling (time-based), then the --warmup count
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        settle_steps += 20
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"[bench] clocks settled ({settle_steps} steps, {settle_ms:.0f} ms); warmup done ({args.warmup} steps)",
+          file=sys.stderr, flush=True)
 
     # Mean launch duration of one kernel: reps back-to-back launches on the
     # launch stream, HIP events around the whole run (an event between two
@@ -164,10 +179,12 @@ def main():
     print(f"[bench] sparse steps done: {ms_step:.4f} ms/step (events {gpu_ms_step:.4f})", file=sys.stderr, flush=True)
 
     # each kernel of the step alone, same lists and tensors
+    # (at least 200 launches whatever --steps says: the roofline is taken from this)
+    n_alone = max(args.steps, 200)
     attn_ms = timed(lambda: vs.attn_fwd(q, k, v, w.sides, w.tile, w.q_scale, kv_cnt, kv_idx, softmax_scale=scale,
-                                        out=o, lse=lse, stream=stream), args.steps)
+                                        out=o, lse=lse, stream=stream), n_alone)
     mask_ms = timed(lambda: vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, radius=w.radii,
-                                          out=(kv_cnt, kv_idx, None), stream=stream), args.steps)
+                                          out=(kv_cnt, kv_idx, None), stream=stream), n_alone)
     print(f"[bench] kernels alone: attn {attn_ms:.4f} ms, mask {mask_ms:.4f} ms", file=sys.stderr, flush=True)
 
     # single launches, warm and cold: HIP events around one attention launch,
@@ -237,6 +254,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"steps": settle_steps, "ms": settle_ms,
+                   "what": "steps run before the --warmup count until this much wall time passed (clock ramp)"},
         "ms_per_step": ms_step,
         "gpu_ms_per_step": gpu_ms_step,
         "higher_is_better": True,
@@ -262,6 +281,7 @@ def main():
                           "tflops": flops / (pair_ms * 1e-3) / 1e12, "vs_64_query_kernel": ref64_ms / pair_ms,
                           "what": "128-query workgroups over pairs of 8x8 query tiles, union chunk walk"},
         "single_launch": single,
+        "attn_kernel_launches_timed": n_alone,
         "roofline": {"bound": "mfma", "achieved": flops / (attn_ms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                      "traffic": TRAFFIC["bytes"] if kernel_sources_sha256() == TRAFFIC["sources_sha256"] else None,
@@ -294,6 +314,10 @@ def main():
     if not args.no_high_res:
         result["high_res"] = bench_high_res(vs, torch, W, SpatialField, to_dev, args, stream, dev)
         print("[bench] high-res done", file=sys.stderr, flush=True)
+
+    if not args.no_sweep:
+        result["budget_sweep"] = bench_budget_sweep(vs, torch, W, SpatialField, to_dev, args, stream, dev)
+        print("[bench] budget sweep done", file=sys.stderr, flush=True)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q_np, k_np, v_np, cnt_h, idx_h, sizes, round_bf16, args.cpu_seconds)
@@ -463,6 +487,74 @@ def bench_high_res(vs, torch, W, SpatialField, to_dev, args, stream, dev):
             "kernel_speedup_vs_dense": dense_ms / attn_ms,
             "count_sparsity": float(1.0 - cnt_h.sum() / (nqb * nkb)), "flop_sparsity": float(1.0 - flops / dense_flops),
             "timed": "mask + attention steps; the attention alone; the dense kernel, HIP events around back-to-back runs"}
+
+
+def bench_budget_sweep(vs, torch, W, SpatialField, to_dev, args, stream, dev):
+    """The 8B-shaped last two scales (B = 2, H = 28, d = 128): queries at side
+    48 (2304 tokens over 6425) and side 64 (4096 over 10521), the CSLA budget
+    mode keeping 75 / 85 / 90 / 95% of the key tiles out of each row.  Per
+    point: the budget mask + attention step, the attention alone, effective
+    TFLOP/s, fraction of the bf16 peak and speedup against the dense kernel on
+    the same tensors (HIP events around back-to-back launches)."""
+    out = []
+    for w in (W.LAST_TWO_8B_48, W.LAST_TWO_8B_64):
+        f = SpatialField(w.seed, w.wid, w.B, w.H, w.d)
+        k_np, v_np = f.keys_values(w.sides[: w.q_scale + 1], w.n_sink, largest_side=w.sides[w.q_scale])
+        q, k, v = to_dev(f.queries(w.sides[w.q_scale])), to_dev(k_np), to_dev(v_np)
+        del k_np, v_np
+        nqb, nkb, nq, nk = vs.geom_counts(w.sides, w.tile, w.q_scale)
+        cnt = torch.empty(nqb, dtype=torch.int32, device=dev)
+        idx = torch.empty(nqb, nkb, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        scale = 1.0 / math.sqrt(w.d)
+        sizes = tile_sizes(w.sides, w.q_scale, w.tile)
+        dense_flops = 4.0 * w.d * nq * nk * w.B * w.H
+
+        def run(fn, warm, reps):
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        dense_ms = run(lambda: vs.dense_attn_fwd(q, k, v, softmax_scale=scale, out=o, want_lse=False, stream=stream),
+                       2, 20)
+        for budget in w.budgets:
+            def mask():
+                vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, budget=budget, out=(cnt, idx, None),
+                              stream=stream)
+
+            def attn():
+                vs.attn_fwd(q, k, v, w.sides, w.tile, w.q_scale, cnt, idx, softmax_scale=scale, out=o,
+                            want_lse=False, stream=stream)
+
+            def step():
+                mask()
+                attn()
+
+            step_ms = run(step, 20, 100)
+            attn_ms = run(attn, 2, 100)
+            mask()
+            torch.cuda.synchronize()
+            cnt_h, idx_h = cnt.cpu().numpy(), idx.cpu().numpy()
+            flops = kept_flops(cnt_h, idx_h, sizes, w.tile * w.tile, w.d, w.B * w.H)
+            tf = flops / (attn_ms * 1e-3) / 1e12
+            out.append({"query_side": w.sides[w.q_scale], "cached_tokens": nk, "budget_tiles": budget,
+                        "count_sparsity": float(1.0 - cnt_h.sum() / (nqb * nkb)),
+                        "flop_sparsity": float(1.0 - flops / dense_flops),
+                        "ms_per_step": step_ms, "attn_kernel_ms": attn_ms, "dense_kernel_ms": dense_ms,
+                        "effective_tflops": flops / (step_ms * 1e-3) / 1e12, "attn_tflops": tf,
+                        "frac_of_peak": tf / PEAK_BF16_TFLOPS, "speedup_vs_dense": dense_ms / step_ms,
+                        "kernel_speedup_vs_dense": dense_ms / attn_ms})
+        del q, k, v, o
+    return {"workload": "last_two_8b (B=2, H=28, d=128, sides 48 and 64, budget mode 75/85/90/95%)", "points": out,
+            "timed": "budget mask + attention steps; the attention alone; the dense kernel, HIP events around "
+                     "back-to-back runs"}
 
 
 def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):

@@ -73,18 +73,40 @@ def test_mapping_bit_exact_on_gpu_selection(cs4a_run, T):
     assert (r["lists"][T][1] == idx).all()
 
 
+def _top_p_margin(row: np.ndarray, p: float) -> float:
+    """How far, in score units, one row's top-p decision is from changing: the
+    gaps between p times the row's mass and the cumulative mass of the kept
+    prefix with and without its last tile, and the gap between the last kept
+    and the first dropped score (a swap there changes the set)."""
+    s = np.sort(row)[::-1]
+    cum = np.cumsum(s)
+    thr = p * cum[-1]
+    k = int(np.argmax(cum >= thr)) + 1          # tiles kept
+    gaps = [cum[k - 1] - thr]
+    if k >= 2:
+        gaps.append(thr - cum[k - 2])
+    if k < s.size:
+        gaps.append(s[k - 1] - s[k])
+    return float(min(gaps))
+
+
 def test_selection_end_to_end(cs4a_run):
-    """Against the oracle's own float64 scores: rows may differ only where the
-    top-p decision is within float32 rounding, and any GPU selection still
-    reaches the mass threshold on the oracle's scores."""
+    """Against the oracle's own float64 scores: a row's selection may differ
+    only where the oracle's decision lies within 1e-5 of a change (its
+    top-p margin, in score units); such rows are counted and reported, and
+    any GPU selection still reaches the mass threshold on the oracle's
+    scores."""
     r = cs4a_run
     w = r["w"]
     ref = OC.block_scores(r["q_d"], r["k"], w.sides, r["D"], w.tile, 1 / math.sqrt(w.d))
     cnt, idx = OC.top_p_select(ref.astype(np.float32), W.CS4A_TOP_P)
     gc, gi = r["sel"]
     diff = np.flatnonzero((cnt != gc).reshape(-1) | (idx != gi).reshape(-1, idx.shape[-1]).any(axis=1))
-    assert diff.size <= max(1, cnt.size // 50), f"{diff.size} of {cnt.size} rows differ"
     flat_ref = ref.reshape(-1, ref.shape[-1])
+    margins = [_top_p_margin(flat_ref[row], W.CS4A_TOP_P) for row in diff]
+    print(f"end-to-end selection: {diff.size} of {cnt.size} rows differ; their margins {margins}")
+    assert all(m < 1e-5 for m in margins), margins
+    assert diff.size <= max(1, cnt.size // 50), f"{diff.size} of {cnt.size} rows differ"
     for row in diff:
         kept = gi.reshape(-1, gi.shape[-1])[row, : gc.reshape(-1)[row]]
         mass = flat_ref[row, kept].sum()

@@ -43,6 +43,34 @@ def test_top_p_hand_fixture():
         assert list(cs4a.top_p_row(np.array(case["scores"], np.float32), case["p"])) == case["kept"], case
 
 
+def _f32_exact(num, exp):
+    """The float32 value num * 2^exp (asserted exact)."""
+    v = np.float32(num * 2.0 ** exp)
+    assert float(v) == num * 2.0 ** exp
+    return v
+
+
+def test_quantise_floors_non_dyadic_scores():
+    """quantise takes the floor of score * 2^24: hand cases whose product has a
+    fractional part (round and ceil give one more)."""
+    fx = json.load(open(GOLDEN))["quantise"]
+    for case in fx["cases"]:
+        got = int(cs4a.quantise(np.array([_f32_exact(case["num"], case["exp"])], np.float32))[0])
+        assert got == case["m"], case
+
+
+def test_top_p_non_dyadic_fixture():
+    """Top-p on scores that are not exact multiples of 2^-24: the threshold
+    uses the float32 value of p (case A) and the floored quantisation decides
+    the order (case B)."""
+    fx = json.load(open(GOLDEN))["top_p_nondyadic"]
+    for case in fx["cases"]:
+        sc = np.array([_f32_exact(n, e) for n, e in zip(case["nums"], case["exps"])], np.float32)
+        assert list(cs4a.top_p_row(sc, case["p"])) == case["kept"], case
+        cnt, idx = cs4a.top_p_select(sc[None, :], case["p"])
+        assert list(idx[0, : cnt[0]]) == case["kept"]
+
+
 def _brute_force_min_size(m, thr):
     n = len(m)
     for size in range(n + 1):
