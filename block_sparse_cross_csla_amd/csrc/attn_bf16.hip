@@ -237,6 +237,11 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 // 16 above the running maximum), far inside the range of bf16 and float.
 constexpr float kSumCap = 65536.0f;
 
+template <bool V>
+struct IntC {
+    static constexpr bool value = V;
+};
+
 // P^T = exp2(S^T c - m) rounded to bf16 (the PV operand), and the lane's sum
 // of the float weights (pairwise).
 __device__ __forceinline__ float exp_chunk(const f32x16& s, float c, float m, bf16x8 (&pt)[2]) {
@@ -256,7 +261,7 @@ __device__ __forceinline__ float exp_chunk(const f32x16& s, float c, float m, bf
 // them (all K rows before S^T, all V^T reads before the softmax, so they land
 // while it runs); scheduling barriers keep the compiler from moving them back
 // next to their uses.
-template <int D>
+template <int D, bool EXACT>
 __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __restrict__ kst,
                                              const char* __restrict__ vst, const Chunk& cc, float c, int lane,
                                              uint32_t tokmask = 0xffffu) {
@@ -316,28 +321,33 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
             if (!(r < cc.nrows && col < cc.ncols && key < cc.nvalid)) sacc[i] = -INFINITY;
         }
     }
-    // online softmax (log2 domain) against the running maximum, with no
-    // maximum taken over the chunk first: when the 16 weights of a lane sum
-    // above kSumCap (or to inf / NaN, as on the first chunk, whose running
-    // maximum is still -1e30) the chunk is redone on a rare path that raises
-    // the running maximum to the chunk's and rescales O and the row sum.  Every
-    // weight of the fast path is below kSumCap, finite in bf16 and float, and
-    // the normalised result is the same softmax.
-    bf16x8 pt[2];
-    float sum = exp_chunk(sacc, c, st.m_run, pt);
-    if (__builtin_amdgcn_ballot_w64(!(sum <= kSumCap))) {
+    // online softmax (log2 domain).  EXACT (a walk's first chunk, and every
+    // chunk of the safe pass): the running maximum is first raised to the
+    // chunk's.  Otherwise the weights are taken
+    // against the running maximum as it stands, with no maximum over the chunk:
+    // weights up to 2^127 are finite in bf16 and float, so the product below
+    // is exact in arithmetic; afterwards, when a query's weights in this chunk
+    // sum above kSumCap, its maximum is raised by the integer ceil(log2 sum) and
+    // O and the row sum scaled by the exact power of two, so later weights start
+    // from at most 1 again.  A weight that overflows (a score more than 127
+    // above the running maximum, log2 domain) leaves inf / NaN behind, which the
+    // kernel detects at the end of the walk and answers with a safe pass.
+    if (EXACT) {
         float mx = sacc[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
         mx = half_swap_max(mx);
         const float m_new = fmaxf(st.m_run, mx * c);
-        const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+        if (__builtin_amdgcn_ballot_w64(m_new > st.m_run)) {
+            const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
 #pragma unroll
-        for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] *= alpha;
-        st.l_run *= alpha;
-        st.m_run = m_new;
-        sum = exp_chunk(sacc, c, st.m_run, pt);
+            for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] *= alpha;
+            st.l_run *= alpha;
+            st.m_run = m_new;
+        }
     }
+    bf16x8 pt[2];
+    const float sum = exp_chunk(sacc, c, st.m_run, pt);
     st.l_run += sum;
     __builtin_amdgcn_sched_barrier(0);
 
@@ -347,6 +357,17 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
 #pragma unroll
         for (int mb = 0; mb < MBLK; ++mb)
             st.oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[mb][t], pt[t], st.oacc[mb], 0, 0, 0);
+
+    if (!EXACT && __builtin_amdgcn_ballot_w64(!(sum <= kSumCap))) {
+        const float sq = half_swap_max(sum);               // both halves of the query agree
+        if (sq > kSumCap && sq <= 3.0e38f) {
+            const int dexp = (int)__builtin_ceilf(__builtin_log2f(sq));
+#pragma unroll
+            for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] *= __builtin_ldexpf(1.0f, -dexp);
+            st.l_run = __builtin_ldexpf(st.l_run, -dexp);
+            st.m_run += (float)dexp;
+        }
+    }
 }
 
 // floor(num / den) for 0 <= num < 2^24, den >= 1 (float estimate, one correction each way)
@@ -524,7 +545,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
 
     // ---- the walk, in table builds of up to kTableCap chunks (the first one
     // before the accumulators are live)
-    Walk w;
+    Walk w, w0;   // w0: the walk as it starts (for the safe pass)
     __shared__ int table_n;
     int nch;
     bool first_loaded = false;   // the first chunk's loads already issued
@@ -534,6 +555,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         w.j = w.cnt = 0;
         w.idx = nullptr;
         nch = (w.cend + 31) >> 5;
+        w0 = w;
     } else {
         const LaneGeom lg = lane_geom(a.g, lane);
         const int64_t row = (a.per_head ? (int64_t)bh * a.nqb : 0) + qt;
@@ -563,6 +585,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         w.cnext = 0;
         w.cend = __builtin_amdgcn_readlane(lg.off, s);
         w.j = __builtin_amdgcn_readlane(lg.tb, s);
+        w0 = w;
         // the run's first chunk is known now: its loads overlap the table build
         if (w.cend > 0) {
             const int nv = min(32, w.cend);
@@ -578,72 +601,120 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         nch = __builtin_amdgcn_readfirstlane(table_n);
     }
 
-#pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] = (f32x16)0.0f;
-    st.m_run = -1e30f;   // finite: a fully masked chunk gives P = 0, not NaN
-    st.l_run = 0.0f;
+    // The walk, in two forms.  The fast form (EXACT false) takes the running
+    // maximum from a walk's first chunk and afterwards takes every chunk's
+    // weights against it, raising it after a chunk whose weights sum above
+    // kSumCap; a weight that overflows (a score more than 127 above the
+    // running maximum, log2 domain) leaves a non-finite value, and both waves
+    // then redo the walk in the exact form, which raises the maximum to each
+    // chunk's before its weights.
+    __shared__ int bad_flag[2];
     TokenState ts;
-    if (TOKEN) token_init(ts, a, lane);
-
-    while (nch > 0) {
-        // descriptors of chunks [win, win + 64) in registers, lane i = chunk win + i
-        int win = 0;
-        uint32_t d0 = 0, d1 = 0;
-        if (!DENSE) {
-            const uint2 t = table[min(lane, kTableCap - 1)];
-            d0 = t.x;
-            d1 = t.y;
-        }
-        auto desc = [&](int ci) -> Chunk {
-            if (DENSE) {
-                const int base = 32 * ci;
-                return unpack_chunk(base, pack_info(8, 4, 8, min(32, w.cend - base)));
+    auto walk = [&](auto exact_tag) {
+        constexpr bool EXACT = decltype(exact_tag)::value;
+        if (EXACT) {   // restart the walk
+            w = w0;
+            if (!DENSE) {
+                if (wave == 0) {
+                    const int nb = build_table(w, a.g, lane_geom(a.g, lane), table, lane);
+                    if (lane == 0) table_n = nb;
+                }
+                __syncthreads();
+                nch = __builtin_amdgcn_readfirstlane(table_n);
+            } else {
+                nch = (w.cend + 31) >> 5;
             }
-            if (ci - win >= 64) {
-                win += 64;
-                const uint2 t = table[min(win + lane, kTableCap - 1)];
+        }
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] = (f32x16)0.0f;
+        st.m_run = -1e30f;   // finite: a fully masked chunk gives P = 0, not NaN
+        st.l_run = 0.0f;
+        if (TOKEN) token_init(ts, a, lane);
+        auto attend = [&](auto ex_tag, const char* kst, const char* vst, const Chunk& cc) {
+            attend_chunk<D, decltype(ex_tag)::value>(st, kst, vst, cc, c, lane,
+                                                     TOKEN ? csla_token_bits(ts, cc, qy, qx, a.q_side, g) : 0xffffu);
+        };
+        int walked = 0;
+        while (nch > 0) {
+            walked += nch;
+            // descriptors of chunks [win, win + 64) in registers, lane i = chunk win + i
+            int win = 0;
+            uint32_t d0 = 0, d1 = 0;
+            if (!DENSE) {
+                const uint2 t = table[min(lane, kTableCap - 1)];
                 d0 = t.x;
                 d1 = t.y;
             }
-            return unpack_chunk((int32_t)__builtin_amdgcn_readlane(d0, ci - win),
-                                __builtin_amdgcn_readlane(d1, ci - win));
-        };
+            auto desc = [&](int ci) -> Chunk {
+                if (DENSE) {
+                    const int base = 32 * ci;
+                    return unpack_chunk(base, pack_info(8, 4, 8, min(32, w.cend - base)));
+                }
+                if (ci - win >= 64) {
+                    win += 64;
+                    const uint2 t = table[min(win + lane, kTableCap - 1)];
+                    d0 = t.x;
+                    d1 = t.y;
+                }
+                return unpack_chunk((int32_t)__builtin_amdgcn_readlane(d0, ci - win),
+                                    __builtin_amdgcn_readlane(d1, ci - win));
+            };
 
-        // two LDS stages, one barrier per chunk: after it, every wave has its
-        // loads of this chunk in LDS and has finished the previous chunk, whose
-        // stage then takes the next prefetch
-        Chunk cur = desc(0), nxt;
-        if (!first_loaded) load_chunk<D>(plan, kh, vh, krb, vrb, cur, L, L + STAGE, wave, lane);
-        first_loaded = false;
-        for (int ci = 0; ci < nch; ci += 2) {
-            wait_vmcnt(0);
-            wg_barrier();
-            if (ci + 1 < nch) {
-                nxt = desc(ci + 1);
-                load_chunk<D>(plan, kh, vh, krb, vrb, nxt, L + 2 * STAGE, L + 3 * STAGE, wave, lane);
+            // two LDS stages, one barrier per chunk: after it, every wave has its
+            // loads of this chunk in LDS and has finished the previous chunk, whose
+            // stage then takes the next prefetch
+            Chunk cur = desc(0), nxt;
+            if (!first_loaded) load_chunk<D>(plan, kh, vh, krb, vrb, cur, L, L + STAGE, wave, lane);
+            first_loaded = false;
+            // chunk ci in stage ci % 2, its successor loaded into the other
+            auto step = [&](auto stage_tag, auto ex_tag, int ci) {
+                constexpr int S = decltype(stage_tag)::value ? 1 : 0;
+                wait_vmcnt(0);
+                wg_barrier();
+                if (ci + 1 < nch) {
+                    nxt = desc(ci + 1);
+                    load_chunk<D>(plan, kh, vh, krb, vrb, nxt, L + 2 * (1 - S) * STAGE, L + (3 - 2 * S) * STAGE,
+                                  wave, lane);
+                }
+                attend(ex_tag, sm + 2 * S * STAGE, sm + (2 * S + 1) * STAGE, cur);
+                cur = nxt;
+            };
+            int ci0 = 0;
+            if (!EXACT && walked == nch) {   // the walk's first two chunks: the first exact
+                step(IntC<false>{}, IntC<true>{}, 0);
+                if (nch > 1) step(IntC<true>{}, IntC<false>{}, 1);
+                ci0 = 2;
             }
-            attend_chunk<D>(st, sm, sm + STAGE, cur, c, lane, TOKEN ? csla_token_bits(ts, cur, qy, qx, a.q_side, g) : 0xffffu);
-            if (ci + 1 >= nch) break;
-            cur = nxt;
-            wait_vmcnt(0);
-            wg_barrier();
-            if (ci + 2 < nch) {
-                nxt = desc(ci + 2);
-                load_chunk<D>(plan, kh, vh, krb, vrb, nxt, L, L + STAGE, wave, lane);
+            for (int ci = ci0; ci < nch; ci += 2) {
+                step(IntC<false>{}, IntC<EXACT>{}, ci);
+                if (ci + 1 >= nch) break;
+                step(IntC<true>{}, IntC<EXACT>{}, ci + 1);
             }
-            attend_chunk<D>(st, sm + 2 * STAGE, sm + 3 * STAGE, cur, c, lane,
-                            TOKEN ? csla_token_bits(ts, cur, qy, qx, a.q_side, g) : 0xffffu);
-            cur = nxt;
+            if (DENSE) break;
+            // long lists: rebuild the table with what remains of the walk
+            __syncthreads();   // every wave done with the table and the stages
+            if (wave == 0) {
+                const int nb = build_table(w, a.g, lane_geom(a.g, lane), table, lane);
+                if (lane == 0) table_n = nb;
+            }
+            __syncthreads();
+            nch = __builtin_amdgcn_readfirstlane(table_n);
         }
-        if (DENSE) break;
-        // long lists: rebuild the table with what remains of the walk
-        __syncthreads();   // every wave done with the table and the stages
-        if (wave == 0) {
-            const int nb = build_table(w, a.g, lane_geom(a.g, lane), table, lane);
-            if (lane == 0) table_n = nb;
-        }
+        // a non-finite value, or a zero row sum after a walk over chunks, asks
+        // for the exact form
+        bool bad = !(__builtin_fabsf(st.l_run) <= 3.0e38f) || (walked > 0 && half_swap_sum(st.l_run) == 0.0f);
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) bad |= !(__builtin_fabsf(st.oacc[mb][i]) <= 3.0e38f);
+        return bad;
+    };
+    {
+        const bool wbad = __builtin_amdgcn_ballot_w64(walk(IntC<false>{})) != 0;
+        __syncthreads();   // every wave done with the stages and the table
+        if (lane == 0) bad_flag[wave] = wbad ? 1 : 0;
         __syncthreads();
-        nch = __builtin_amdgcn_readfirstlane(table_n);
+        if (bad_flag[0] | bad_flag[1]) walk(IntC<true>{});
     }
 
     // ---- epilogue
@@ -948,7 +1019,7 @@ __global__ __launch_bounds__(256, 2) void attn_pair_bf16_kernel(const AttnArgs a
                     load_chunk_pair<D>(plan, kh, vh, krb, vrb, ring[nu], L + 2 * nu * STAGE,
                                        L + (2 * nu + 1) * STAGE, wave, lane);
                 }
-                if (own[u] & mine) attend_chunk<D>(st, sm + 2 * u * STAGE, sm + (2 * u + 1) * STAGE, ring[u], c, lane);
+                if (own[u] & mine) attend_chunk<D, true>(st, sm + 2 * u * STAGE, sm + (2 * u + 1) * STAGE, ring[u], c, lane);
             }
         }
         // long walks: rebuild the table with what remains

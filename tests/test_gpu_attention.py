@@ -274,6 +274,52 @@ def test_bf16_large_scores_lazy_rescale(gain):
     _compare(od, lsed, rdo, rdl, BF16_TOL, f"large scores dense gain={gain}")
 
 
+@pytest.mark.parametrize("case", ["underflow", "overflow"])
+def test_bf16_extreme_score_ranges_every_kernel(case):
+    """Scores outside the fast softmax form's range, so that it hands over to
+    the exact form.  underflow: every score of every row about -130 or lower
+    in the log2 domain (all weights against the starting maximum 0 flush to
+    zero); overflow: the keys of one query-scale tile score about 160 above
+    the rest (weights past 2^127).  Sparse, dense and token-exact kernels
+    against the float64 oracle."""
+    vs = _vs()
+    sides, qs, t = SCHEDULE_13, 10, 8
+    B, H, d = 1, 2, 128
+    nqb, nkb, nq, nk = G.counts(sides, qs, t)
+    rng = np.random.default_rng(77)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    from varsparse_inputs import round_bf16
+    q = 32.0 * u + 0.05 * rng.standard_normal((B, H, nq, d))
+    k = rng.standard_normal((B, H, nk, d))
+    if case == "underflow":
+        k = k - 32.0 * u
+    else:
+        off = G.scale_offsets(sides)[qs]
+        side = sides[qs]
+        toks = [off + y * side + x for y in range(8, 16) for x in range(16, 24)]   # one query-scale tile
+        k[:, :, toks] = 40.0 * u + 0.1 * rng.standard_normal((B, H, len(toks), d))
+    v = rng.standard_normal((B, H, nk, d))
+    q, k, v = round_bf16(q.astype(np.float32)), round_bf16(k.astype(np.float32)), round_bf16(v.astype(np.float32))
+    cnt, idx, _ = vs.build_mask(sides, t, qs, 5, radius=(2,) * (qs + 1))
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    o, lse = vs.attn_fwd(qd, kd, vd, sides, t, qs, cnt, idx)
+    od, lsed = vs.dense_attn_fwd(qd, kd, vd)
+    ot, lset = vs.attn_fwd_token(qd, kd, vd, sides, t, qs, 5, (2,) * (qs + 1), cnt, idx)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    q64, k64, v64 = q.astype(np.float64), k.astype(np.float64), v.astype(np.float64)
+    mc, mi = lists(oracle_mask(sides, qs, t, 5, (2,) * (qs + 1)))
+    ro, rl = OA.block_sparse_attention(q64, k64, v64, sides, qs, t, mc, mi, scale)
+    _compare(o, lse, ro, rl, BF16_TOL, f"{case} sparse")
+    rows = np.arange(0, nq, 29)
+    rdo, rdl = OA.dense_attention(q64, k64, v64, scale, q_rows=rows)
+    _compare(od, lsed, rdo, rdl, BF16_TOL, f"{case} dense")
+    rto, rtl = OA.token_masked_attention(q64, k64, v64, sides, qs, t, 5, (2,) * (qs + 1), scale,
+                                         q_tiles=range(0, nqb, 5))
+    _compare(ot, lset, rto, rtl, BF16_TOL, f"{case} token-exact")
+
+
 def test_odd_head_count_every_tile_all_list_kernels():
     """B=1, H=3: the dispatch order interleaves the work items of head pairs
     and ranks each head's query tiles by list length, so the last pair holds
