@@ -2,10 +2,12 @@
 
 Source: SparVAR, ai.info summary, "Methodology in Plain English" (the second
 module, CSLA) and "Main Findings" (the sink ablation: sink = scales <= 5,
-window sizes 3/5/7).  Each query token of a high-resolution scale is projected
-onto the coordinate grid of every earlier scale; a key is kept only inside a
-per-scale window around the projection; a separate sink mask keeps the early
-scales visible to every query; the token mask is then aggregated into blocks.
+window sizes 3/5/7).  What the module computes, in this implementation's
+terms: the position of a query of a late scale is carried onto every coarser
+grid; on each of those grids only the keys close to that position survive;
+every key of the first few ("sink") scales survives for every query; and
+the surviving token pairs decide which (query block, key block) pairs are
+computed.
 
 Readings taken where the pages leave a step open:
 

@@ -6,8 +6,8 @@ scale and of scale k itself.  Here the key/value cache of a query scale q is
 the concatenation of scales 0..q, each scale a side x side grid in raster
 (row-major) order.
 
-Blocks ("this token-wise mask is then aggregated into blocks", ai.info,
-"Methodology in Plain English") are read as square t x t tiles of one scale's
+The block mask the pages derive from the token mask (ai.info, "Methodology in
+Plain English") is read here with blocks as square t x t tiles of one scale's
 grid; tiles on the right/bottom edge of a grid whose side is not a multiple of
 t are partial.  Key tiles are numbered scale by scale, raster order within a
 scale; query tiles are numbered in raster order over the query scale.

@@ -2,10 +2,11 @@
 to correct its sparse attention output (oracle; test infrastructure).
 
 Source: SparVAR, ai.info summary, "Methodology in Plain English" (the first
-module, CS4A: the output left over at the decision scale is kept as a cache
-and upsampled to correct the later scales' sparse outputs) and "Main
-Findings" (the item on the two modules' increments: adding the cached
-decision-scale output raises PSNR at almost no cost).
+module, CS4A) and "Main Findings" (the item on the two modules' increments).
+In this implementation's terms: at the decision scale, the part of the full
+attention output that the sparse selection misses is stored; it is enlarged
+to each later scale's grid and added to that scale's sparse output (the
+pages credit it with a PSNR gain at negligible cost).
 
 Readings taken where the pages leave a step open:
 

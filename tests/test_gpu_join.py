@@ -9,10 +9,13 @@ the union (or intersection) of the GPU's CS4A lists and the oracle's CSLA
 window mask.  The loop itself (decision scale side 32: full and sparse
 attention, scores, selection; each later scale: mapping, CSLA window mask,
 union, block-sparse attention, O_cache correction) is compared with the
-oracle's loop on two heads: lists bit-exact, outputs within 6e-2, the sum of
-the bf16 output bound (2e-2) of the three attention outputs entering each
-corrected value (the target's sparse output, the decision scale's full and
-sparse outputs)."""
+oracle two ways on two heads.  Stage by stage: each target's corrected output
+against the oracle's block-sparse attention over the GPU's own joined lists,
+corrected with the GPU's own decision-scale outputs, within the bf16 bar
+2e-2.  End to end, against the oracle's loop from the inputs: lists
+bit-exact, outputs within 6e-2, the sum of the bf16 output bound of the
+three attention outputs entering each corrected value (the target's sparse
+output, the decision scale's full and sparse outputs)."""
 import math
 
 import numpy as np
@@ -130,6 +133,48 @@ def test_full_size_joined_lists(join):
         ec, ei = L.lists_from_mask(S.join_masks(cs4a, win, join))
         assert np.array_equal(jc.cpu().numpy(), ec), T
         assert np.array_equal(ji.cpu().numpy(), ei), T
+
+
+def test_scale_loop_stage_by_stage():
+    """Each target scale's corrected output, given the GPU's own upstream
+    results: the oracle's block-sparse attention over the GPU's joined lists,
+    plus the nearest-upsampled residual of the GPU's decision-scale full and
+    sparse outputs (the oracle's O_cache correction), within 2e-2."""
+    from oracle import attention as OA, ocache as OO
+    vs = _vs()
+    w = W.CS4A
+    D = W.CS4A_DECISION
+    B, H = 1, 2
+    n = len(w.sides)
+    scale = 1 / math.sqrt(w.d)
+    f = SpatialField(w.seed, w.wid, B, H, w.d)
+    k, v = f.keys_values(w.sides, w.n_sink)
+    k, v = round_bf16(k), round_bf16(v)
+    qs = [round_bf16(f.queries(s)) for s in w.sides]
+    off = G.scale_offsets(w.sides)
+    kd, vd = to_device(k), to_device(v)
+    qd = [to_device(x) for x in qs]
+    nkD = off[D + 1]
+    o_full, _ = vs.dense_attn_fwd(qd[D], kd[:, :, :nkD], vd[:, :, :nkD], softmax_scale=scale, want_lse=False)
+    scores, _, _, dc, di = vs.map_indices(w.sides, w.tile, D, D, w.n_sink, W.CS4A_TOP_P, q_d=qd[D], k=kd)
+    o_sparse, _ = vs.attn_fwd(qd[D], kd[:, :, :nkD], vd[:, :, :nkD], w.sides, w.tile, D, dc, di,
+                              softmax_scale=scale, want_lse=False)
+    of = o_full.float().cpu().numpy().astype(np.float64)
+    osp = o_sparse.float().cpu().numpy().astype(np.float64)
+    for T in W.CS4A_TARGETS:
+        _, _, _, kc, ki = vs.map_indices(w.sides, w.tile, D, T, w.n_sink, W.CS4A_TOP_P, scores=scores)
+        mc, mi, _ = vs.build_mask(w.sides, w.tile, T, w.n_sink, radius=vs.window_radius(n, T, WINDOWS))
+        jc, ji = vs.join_lists(kc, ki, mc, mi, join="union")
+        nkT = off[T + 1]
+        o, _ = vs.attn_fwd(qd[T], kd[:, :, :nkT], vd[:, :, :nkT], w.sides, w.tile, T, jc, ji,
+                           softmax_scale=scale, want_lse=False)
+        vs.ocache_correct(o_full, o_sparse, o, w.sides[D], w.sides[T])
+        torch.cuda.synchronize()
+        ro, _ = OA.block_sparse_attention(qs[T], k[:, :, :nkT], v[:, :, :nkT], w.sides, T, w.tile,
+                                          jc.cpu().numpy(), ji.cpu().numpy(), scale)
+        want = OO.correct(ro, of, osp, w.sides[D], w.sides[T])
+        err = np.abs(o.float().cpu().numpy() - want).max()
+        assert err <= 2e-2, (T, err)
 
 
 def test_scale_loop_matches_oracle():
