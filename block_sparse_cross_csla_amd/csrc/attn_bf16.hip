@@ -23,10 +23,15 @@
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T held in
 //    registers for the whole walk), so that every lane holds the scores of a
 //    single query: the row max needs one v_permlane32_swap, row sums none;
-//  * online softmax in the exp2 domain against the running maximum: the
-//    chunk's own maximum is taken only on a rare path, when a weight would
-//    exceed 2^16 (exact in arithmetic: the final normalisation uses the same
-//    running maximum);
+//  * online softmax in the exp2 domain against a running maximum set by the
+//    walk's first chunk: later chunks' weights go to the PV product with no
+//    maximum over the chunk; a query whose weights in a chunk sum above 2^16
+//    then has its maximum raised by ceil(log2 sum) and O and the row sum
+//    scaled by that exact power of two; a weight that overflows leaves a
+//    non-finite value, found at the end of the walk, which is then redone in
+//    an exact form that raises the maximum to each chunk's before its weights
+//    (exact in arithmetic either way: the final normalisation uses the same
+//    running maximum as the weights);
 //  * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T
 //    accumulator registers (no data movement), V^T is read from LDS with
 //    gfx950's transposing ds_read_b64_tr_b16.
