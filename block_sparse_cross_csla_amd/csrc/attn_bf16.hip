@@ -226,7 +226,43 @@ struct WaveState {
     bf16x8 qreg[D / 16];          // B operand of S^T = K Q^T (this lane's query)
     f32x16 oacc[D / 32];          // O^T accumulator
     float m_run, l_run;           // running max (log2 domain) and this lane's partial sum
+    // this lane's byte offsets, within a stage, of its MFMA operand reads:
+    // K rows (one per k-step) and V^T (transposing reads); a stage's own
+    // offset is a compile-time constant added to them, which the LDS reads
+    // take as their immediate offset
+    uint32_t koff[D / 16];
+    uint32_t voff[D / 32][2][2];
 };
+
+// Fill the operand-read offsets of WaveState (once per kernel).  The values
+// are made opaque to the compiler so that it keeps one register per read
+// and adds each stage's constant in the instruction, instead of splitting
+// them into a row part and a unit part that it re-adds for every chunk.
+template <int D>
+__device__ __forceinline__ void init_lds_offsets(WaveState<D>& st, int lane) {
+    constexpr int ROWB = D * 2, CH = D / 8;
+    const int n = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+        st.koff[s] = (uint32_t)(n * ROWB + (((2 * s + g) ^ swz<CH>(n)) << 4));
+        asm volatile("" : "+v"(st.koff[s]));
+    }
+    const int c16 = lane >> 4, p16 = lane & 15;
+    const int hf = c16 & 1, r4 = p16 >> 2, q4 = p16 & 3;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) {
+        const int d = 32 * mb + 16 * hf + 4 * q4;
+        const int lc = d >> 3, within = (d & 7) * 2;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int row = 16 * t + 8 * jj + 4 * g + r4;
+                st.voff[mb][t][jj] = (uint32_t)(row * ROWB + ((lc ^ swz<CH>(row)) << 4) + within);
+                asm volatile("" : "+v"(st.voff[mb][t][jj]));
+            }
+    }
+}
 
 // max / sum of a value and its partner lane (lane ^ 32) via v_permlane32_swap
 __device__ __forceinline__ float half_swap_max(float x) {
@@ -279,10 +315,7 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
     // S^T (32 keys x 32 queries) = K Q^T
     bf16x8 kop[KSTEPS];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        const int pc = (2 * s + g) ^ swz<CH>(n);
-        kop[s] = *(const bf16x8*)(kst + n * ROWB + pc * 16);
-    }
+    for (int s = 0; s < KSTEPS; ++s) kop[s] = *(const bf16x8*)(kst + st.koff[s]);
     __builtin_amdgcn_sched_barrier(0);
     f32x16 sacc = (f32x16)0.0f;
 #pragma unroll
@@ -290,20 +323,15 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
     __builtin_amdgcn_sched_barrier(0);
 
     // V^T operands for the whole chunk (transposing LDS reads), in flight during the softmax
-    const int c16 = lane >> 4, p16 = lane & 15;
-    const int half = c16 & 1, r4 = p16 >> 2, q4 = p16 & 3;
     bf16x8 vop[MBLK][2];
 #pragma unroll
     for (int mb = 0; mb < MBLK; ++mb) {
-        const int d = 32 * mb + 16 * half + 4 * q4;
-        const int lc = d >> 3, within = (d & 7) * 2;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             bf16x4 part[2];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-                const int row = 16 * t + 8 * jj + 4 * g + r4;
-                const char* addr = vst + row * ROWB + ((lc ^ swz<CH>(row)) << 4) + within;
+                const char* addr = vst + st.voff[mb][t][jj];
                 part[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                     (__attribute__((address_space(3))) bf16x4*)(addr));
             }
@@ -545,6 +573,7 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     const __bf16* qp = a.q + b * a.sq_b + h * a.sq_h + tok * a.sq_t;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) st.qreg[s] = *(const bf16x8*)(qp + 16 * s + 8 * g);
+    init_lds_offsets<D>(st, lane);
     LoadPlan<D> plan;
     make_plan<D>(plan, wave, lane, a.sk_t, a.sv_t);
 
@@ -963,6 +992,7 @@ __global__ __launch_bounds__(256, 2) void attn_pair_bf16_kernel(const AttnArgs a
     const __bf16* qp = a.q + b * a.sq_b + h * a.sq_h + tok * a.sq_t;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) st.qreg[s] = *(const bf16x8*)(qp + 16 * s + 8 * g);
+    init_lds_offsets<D>(st, lane);
 #pragma unroll
     for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] = (f32x16)0.0f;
     st.m_run = -1e30f;
