@@ -231,7 +231,7 @@ struct WaveState {
     // offset is a compile-time constant added to them, which the LDS reads
     // take as their immediate offset
     uint32_t koff[D / 16];
-    uint32_t voff[D / 32][2][2];
+    uint32_t voff[D / 32][2];     // rows 16 t + ..: the swizzle repeats every 16 rows, so t adds 16 rows
 };
 
 // Fill the operand-read offsets of WaveState (once per kernel).  The values
@@ -254,13 +254,11 @@ __device__ __forceinline__ void init_lds_offsets(WaveState<D>& st, int lane) {
         const int d = 32 * mb + 16 * hf + 4 * q4;
         const int lc = d >> 3, within = (d & 7) * 2;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int row = 16 * t + 8 * jj + 4 * g + r4;
-                st.voff[mb][t][jj] = (uint32_t)(row * ROWB + ((lc ^ swz<CH>(row)) << 4) + within);
-                asm volatile("" : "+v"(st.voff[mb][t][jj]));
-            }
+        for (int jj = 0; jj < 2; ++jj) {
+            const int row = 8 * jj + 4 * g + r4;
+            st.voff[mb][jj] = (uint32_t)(row * ROWB + ((lc ^ swz<CH>(row)) << 4) + within);
+            asm volatile("" : "+v"(st.voff[mb][jj]));
+        }
     }
 }
 
@@ -331,7 +329,7 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
             bf16x4 part[2];
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-                const char* addr = vst + st.voff[mb][t][jj];
+                const char* addr = vst + 16 * t * (2 * D) + st.voff[mb][jj];
                 part[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                     (__attribute__((address_space(3))) bf16x4*)(addr));
             }
@@ -401,6 +399,171 @@ __device__ __forceinline__ void attend_chunk(WaveState<D>& st, const char* __res
             st.m_run += (float)dexp;
         }
     }
+}
+
+// ---- the pipelined chunk step of the 64-query walk
+//
+// One step takes chunk c's scores (K reads, S^T = K Q^T, masks) and then, in
+// one scheduling region, chunk c - 1's product O^T += V^T P^T (its weights and
+// V^T operands carried in registers from the previous step) interleaved with
+// chunk c's weights, so that the wave's own MFMAs and softmax VALU overlap
+// instead of running back to back.  Chunk c's V^T operands are read last, for
+// its product in the next step.  A raise of the running maximum decided from
+// chunk c's weights (the fast form) scales O^T after chunk c's product, i.e.
+// in the next step or in the drain; the exact form scales O^T (after chunk
+// c - 1's product) before chunk c's product.  A segment's first step takes a
+// zero product (zero weights and zero V^T operands).
+template <int D>
+struct PipeState {
+    bf16x8 pt[2];              // P^T of the chunk whose product is pending
+    bf16x8 vop[D / 32][2];     // its V^T operands
+    float pend;                // scale for O^T once that product is in (1: none)
+};
+
+template <int D, bool EXACT>
+__device__ __forceinline__ void pipe_chunk(WaveState<D>& st, PipeState<D>& ps, const char* __restrict__ kst,
+                                           const char* __restrict__ vst, const Chunk& cc, float c, int lane,
+                                           uint32_t tokmask) {
+    constexpr int KSTEPS = D / 16;
+    constexpr int MBLK = D / 32;
+    const int g = lane >> 5;
+
+    // S^T (32 keys x 32 queries) = K Q^T, the K operands read in two halves
+    // (the second half's reads overlap the first half's MFMAs)
+    constexpr int KH = KSTEPS / 2;
+    f32x16 sacc = (f32x16)0.0f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        bf16x8 kop[KH];
+#pragma unroll
+        for (int s = 0; s < KH; ++s) kop[s] = *(const bf16x8*)(kst + st.koff[KH * hh + s]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < KH; ++s)
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s], st.qreg[KH * hh + s], sacc, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (tokmask != 0xffffu) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (!((tokmask >> i) & 1u)) sacc[i] = -INFINITY;
+    }
+    if (!cc.full) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = i >> 2, col = 4 * g + (i & 3), key = 8 * r + col;
+            if (!(r < cc.nrows && col < cc.ncols && key < cc.nvalid)) sacc[i] = -INFINITY;
+        }
+    }
+    float alpha = 1.0f;
+    if (EXACT) {   // raise the running maximum to the chunk's first
+        float mx = sacc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+        mx = half_swap_max(mx);
+        const float m_new = fmaxf(st.m_run, mx * c);
+        alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+        st.m_run = m_new;
+    }
+
+    // chunk c - 1's product interleaved with chunk c's weights
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c, -st.m_run));
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb)
+            st.oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ps.vop[mb][t], ps.pt[t], st.oacc[mb], 0, 0, 0);
+    bf16x8 pt[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pt[i >> 3][i & 7] = (__bf16)p[i];
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = p[2 * i] + p[2 * i + 1];
+    float sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+    // the weights are computed here, beside the product, not sunk toward
+    // their later uses
+    asm volatile("" : "+v"(sum), "+v"(pt[0]), "+v"(pt[1]));
+    // one MFMA, then a share of the weights' VALU work (16 fma, 16 exp, 8
+    // packs, 15 adds), 2 MBLK times
+#pragma unroll
+    for (int k = 0; k < 2 * MBLK; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 56 / (2 * MBLK), 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // V^T operands of chunk c (transposing LDS reads), for its product in the next step
+    // (chunk c - 1's product has read the registers they replace)
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            bf16x4 part[2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                part[jj] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4*)(vst + 16 * t * (2 * D) + st.voff[mb][jj]));
+            ps.vop[mb][t] = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (EXACT) {
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+            for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] *= alpha;
+        }
+        st.l_run = st.l_run * alpha + sum;
+    } else {
+        if (__builtin_amdgcn_ballot_w64(ps.pend != 1.0f)) {
+#pragma unroll
+            for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] *= ps.pend;
+        }
+        st.l_run += sum;
+        ps.pend = 1.0f;
+        if (__builtin_amdgcn_ballot_w64(!(sum <= kSumCap))) {
+            const float sq = half_swap_max(sum);               // both halves of the query agree
+            if (sq > kSumCap && sq <= 3.0e38f) {
+                const int dexp = (int)__builtin_ceilf(__builtin_log2f(sq));
+                st.l_run = __builtin_ldexpf(st.l_run, -dexp);
+                st.m_run += (float)dexp;
+                ps.pend = __builtin_ldexpf(1.0f, -dexp);
+            }
+        }
+    }
+
+    ps.pt[0] = pt[0];
+    ps.pt[1] = pt[1];
+}
+
+// No pending product: zero weights against zero V^T operands (a segment's
+// first step then adds nothing to O^T).
+template <int D>
+__device__ __forceinline__ void pipe_reset(PipeState<D>& ps) {
+    const bf16x8 z = (bf16x8)(__bf16)0.0f;
+    ps.pt[0] = ps.pt[1] = z;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb) ps.vop[mb][0] = ps.vop[mb][1] = z;
+    ps.pend = 1.0f;
+}
+
+// The pending product and O^T scale at the end of a walk segment.
+template <int D>
+__device__ __forceinline__ void pipe_drain(WaveState<D>& st, PipeState<D>& ps) {
+    constexpr int MBLK = D / 32;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb)
+            st.oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ps.vop[mb][t], ps.pt[t], st.oacc[mb], 0, 0, 0);
+    if (__builtin_amdgcn_ballot_w64(ps.pend != 1.0f)) {
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] *= ps.pend;
+    }
+    pipe_reset<D>(ps);
 }
 
 // floor(num / den) for 0 <= num < 2^24, den >= 1 (float estimate, one correction each way)
@@ -664,9 +827,11 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         st.m_run = -1e30f;   // finite: a fully masked chunk gives P = 0, not NaN
         st.l_run = 0.0f;
         if (TOKEN) token_init(ts, a, lane);
+        PipeState<D> ps;
+        pipe_reset<D>(ps);
         auto attend = [&](auto ex_tag, const char* kst, const char* vst, const Chunk& cc) {
-            attend_chunk<D, decltype(ex_tag)::value>(st, kst, vst, cc, c, lane,
-                                                     TOKEN ? csla_token_bits(ts, cc, qy, qx, a.q_side, g) : 0xffffu);
+            pipe_chunk<D, decltype(ex_tag)::value>(st, ps, kst, vst, cc, c, lane,
+                                                   TOKEN ? csla_token_bits(ts, cc, qy, qx, a.q_side, g) : 0xffffu);
         };
         int walked = 0;
         while (nch > 0) {
@@ -700,10 +865,14 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
             Chunk cur = desc(0), nxt;
             if (!first_loaded) load_chunk<D>(plan, kh, vh, krb, vrb, cur, L, L + STAGE, wave, lane);
             first_loaded = false;
-            // chunk ci in stage ci % 2, its successor loaded into the other
+            // chunk ci in stage ci % 2, its successor loaded into the other;
+            // chunk ci's product is taken in the step of chunk ci + 1 (or in
+            // the drain after the segment's last chunk)
             auto step = [&](auto stage_tag, auto ex_tag, int ci) {
                 constexpr int S = decltype(stage_tag)::value ? 1 : 0;
-                wait_vmcnt(0);
+                // this wave's loads of chunk ci, and its V^T reads of chunk ci - 1 (whose
+                // stage the loads issued below overwrite), are complete on both waves
+                wait_all();
                 wg_barrier();
                 if (ci + 1 < nch) {
                     nxt = desc(ci + 1);
@@ -719,11 +888,13 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
                 if (nch > 1) step(IntC<true>{}, IntC<false>{}, 1);
                 ci0 = 2;
             }
-            for (int ci = ci0; ci < nch; ci += 2) {
+            int ci = ci0;
+            for (; ci + 1 < nch; ci += 2) {   // whole pairs: the loop has one exit
                 step(IntC<false>{}, IntC<EXACT>{}, ci);
-                if (ci + 1 >= nch) break;
                 step(IntC<true>{}, IntC<EXACT>{}, ci + 1);
             }
+            if (ci < nch) step(IntC<false>{}, IntC<EXACT>{}, ci);
+            pipe_drain<D>(st, ps);
             if (DENSE) break;
             // long lists: rebuild the table with what remains of the walk
             __syncthreads();   // every wave done with the table and the stages
