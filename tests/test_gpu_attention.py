@@ -10,7 +10,7 @@ import torch
 
 from oracle import attention as OA, geometry as G
 from tests._common import gaussian, lists, oracle_mask, spatial, to_device
-from varsparse_inputs import SCHEDULE_13, workloads as W
+from varsparse_inputs import SCHEDULE_13, SCHEDULE_16, round_bf16, workloads as W
 
 pytestmark = pytest.mark.gpu
 
@@ -383,3 +383,53 @@ def test_more_than_64_tiles_per_head_every_tile():
         o, lse = fn(qd, kd, vd, sides, t, qs, cd, idd)
         torch.cuda.synchronize()
         _compare(o, lse, ro, rl, BF16_TOL, f"144 tiles {name}")
+
+
+@pytest.mark.parametrize("growth,spike", [(0.0, False), (6.0, False), (0.0, True)])
+def test_long_lists_split_the_walk(growth, spike):
+    """High-resolution geometry (16 scales, 672 key tiles, 42521 tokens): rows
+    far longer than one chunk table (a full row, one contiguous run of 1329
+    chunks; every other tile, no run past tile 0; a random tenth; an empty
+    row), so that the walk is split into several table builds and each split
+    takes the pending product of its last chunk.  With growth, key norms rise
+    along the cache (x 7 at its end), so that later chunks' weights run far
+    above the running maximum and it is raised many times, also right at the
+    splits.  With spike, the 32 keys of the full row's chunk 511 (the last of
+    its first table build) are scaled by 8, so that most of that row's
+    queries raise their maximum on exactly that chunk and the split's drain
+    applies the pending rescale (57 of tile 0's 64 queries, replaying the
+    rule on the CPU).  The token-masked dense baseline (no lists: every key
+    tile, the token rule applied) walks the same long rows."""
+    vs = _vs()
+    sides, qs, t = SCHEDULE_16, 15, 8
+    B, H, d = 1, 2, 128
+    nqb, nkb, nq, nk = G.counts(sides, qs, t)
+    rng = np.random.default_rng(41)
+    keep = rng.random((B, H, nqb, nkb)) < 0.1
+    keep[0, 0, 0] = True            # the whole cache: one run
+    keep[0, 0, 1] = False
+    keep[0, 0, 1, ::2] = True       # every other tile
+    keep[0, 0, 2] = False           # empty
+    keep[0, 1, 5] = True
+    cnt, idx = lists(keep)
+    q, k, v = gaussian(9, 73, B, H, nq, nk, d)
+    if growth:
+        k = round_bf16(k * (1.0 + growth * np.arange(nk) / nk)[None, None, :, None])
+    if spike:
+        k = k.copy()
+        k[:, :, 511 * 32: 512 * 32] *= 8.0
+        k = round_bf16(k)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    o, lse = vs.attn_fwd(qd, kd, vd, sides, t, qs, torch.from_numpy(cnt).cuda(), torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    tiles = [0, 1, 2, 5, 100, 255]
+    scale = 1 / math.sqrt(d)
+    ro, rl = OA.block_sparse_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                       sides, qs, t, cnt, idx, scale, q_tiles=tiles)
+    _compare(o, lse, ro, rl, BF16_TOL, f"long lists, growth {growth}, spike {spike}")
+    n_sink, radius = 5, [2] * (qs + 1)
+    ot, lt = vs.attn_fwd_token(qd, kd, vd, sides, t, qs, n_sink, radius)
+    torch.cuda.synchronize()
+    rto, rtl = OA.token_masked_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                         sides, qs, t, n_sink, radius, scale, q_tiles=[0, 37, 255])
+    _compare(ot, lt, rto, rtl, BF16_TOL, f"token-masked dense, long rows, growth {growth}, spike {spike}")
