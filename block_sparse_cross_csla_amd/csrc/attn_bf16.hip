@@ -34,7 +34,10 @@
 //    running maximum as the weights);
 //  * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T
 //    accumulator registers (no data movement), V^T is read from LDS with
-//    gfx950's transposing ds_read_b64_tr_b16.
+//    gfx950's transposing ds_read_b64_tr_b16;
+//  * the 64-query walk is pipelined by one chunk: chunk c - 1's PV MFMAs are
+//    interleaved with chunk c's softmax in one scheduling region, so that a
+//    wave's own MFMA and VALU work overlap (see pipe_chunk).
 #include "kernel_args.h"
 
 namespace vs {
