@@ -120,8 +120,16 @@ __device__ __forceinline__ int build_table(Walk& w, const DevGeom& g, const Lane
         const int e = w.j + lane;
         const bool valid = e < w.cnt;
         const int from_regs = __builtin_amdgcn_ds_bpermute((e & 63) << 2, first64);
-        int id = 0;
-        if (valid) id = (have_first64 && e < 64) ? from_regs : (w.idx != nullptr ? w.idx[e] : e);   // no list: every tile
+        int id = e;   // no list: every tile
+        if (have_first64 && e < 64) id = from_regs;
+        else if (valid && w.idx != nullptr) {
+            id = w.idx[e];
+            // consumed here: the wait for this load stays on this path (an
+            // unconditional wait after the branch would also wait for the
+            // first chunk's LDS-DMA loads issued before the table build)
+            asm volatile("" : "+v"(id));
+        }
+        if (!valid) id = 0;
         id = min(max(id, 0), n_tiles - 1);
         int tb = 0, side = __builtin_amdgcn_readlane(lg.side, 0), off = 0, nb = __builtin_amdgcn_readlane(lg.nb, 0);
         for (int s = 1; s < g.n_scales; ++s) {
@@ -650,13 +658,15 @@ __device__ __forceinline__ uint32_t csla_token_bits(TokenState& ts, const Chunk&
 // total order), so all agree on one permutation.  Heads with more than 64
 // query tiles, and walks without a list, keep the natural order.
 // PAIRS: the items are pairs of query tiles (2i, 2i + 1), ranked by the sum of
-// their two list lengths.
+// their two list lengths.  Returns whether the items were ranked; then (not
+// PAIRS) `count` is the list count of the chosen tile as stored, read from
+// the lanes that ranked it.
 template <bool PAIRS = false>
-__device__ __forceinline__ void work_tile(const AttnArgs& a, int work, int nqt, int lane, int* keys, int& bh,
-                                          int& qt) {
+__device__ __forceinline__ bool work_tile(const AttnArgs& a, int work, int nqt, int lane, int* keys, int& bh,
+                                          int& qt, int& count) {
     bh = work / nqt;
     qt = work - bh * nqt;
-    if (a.kv_cnt == nullptr || nqt > 64) return;
+    if (a.kv_cnt == nullptr || nqt > 64) return false;
     const int n_bh = a.B * a.H;
     const int pair = bh >> 1;
     const int j = work - 2 * pair * nqt;               // place within the pair's items
@@ -665,13 +675,14 @@ __device__ __forceinline__ void work_tile(const AttnArgs& a, int work, int nqt, 
     const int r = two ? (j >> 1) : j;                  // wanted rank within the head
     const int32_t* cnt = a.kv_cnt + (a.per_head ? (int64_t)head * a.nqb : 0);
     // distinct keys, larger = earlier: the list length (clamped), then the lower item id
-    int len = 0;
+    int len = 0, raw = 0;
     if (lane < nqt) {
         if (PAIRS) {
             len = max(cnt[2 * lane], 0);
             if (2 * lane + 1 < a.nqb) len += max(cnt[2 * lane + 1], 0);
         } else {
-            len = max(cnt[lane], 0);
+            raw = cnt[lane];
+            len = max(raw, 0);
         }
     }
     const int key = lane < nqt ? min(len, (1 << 24) - 1) * 64 + (63 - lane) : -1;
@@ -685,6 +696,8 @@ __device__ __forceinline__ void work_tile(const AttnArgs& a, int work, int nqt, 
     const uint64_t hit = __ballot(lane < nqt && rank == r);
     bh = head;
     qt = __builtin_ctzll(hit);
+    count = __builtin_amdgcn_readlane(raw, qt);
+    return true;
 }
 
 template <int D, bool DENSE, bool TOKEN>
@@ -701,12 +714,16 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     const int64_t nqt = DENSE ? (a.nq + 63) / 64 : a.nqb;
     const int work = xcd_remap(blockIdx.x, gridDim.x);
     int bh, qt;
+    LaneGeom lg;
+    int ranked_count = 0;
+    bool ranked = false;
     if (DENSE) {
         bh = work / nqt;
         qt = work - bh * nqt;
     } else {
+        lg = lane_geom(a.g, lane);   // independent of the item: in flight during the ranking
         __shared__ __attribute__((aligned(16))) int rank_keys[2][64];
-        work_tile(a, work, nqt, lane, rank_keys[wave], bh, qt);
+        ranked = work_tile(a, work, nqt, lane, rank_keys[wave], bh, qt, ranked_count);
         bh = __builtin_amdgcn_readfirstlane(bh);
         qt = __builtin_amdgcn_readfirstlane(qt);
     }
@@ -734,7 +751,23 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     const lds_ptr L = (lds_ptr)smem;
     const char* sm = smem;
 
-    // Q^T operands first: their loads are in flight while the walk is set up
+    // The list count and the first 64 list entries are loaded before the Q^T
+    // operands, so that waiting for the entries does not wait for Q (vector
+    // loads complete in issue order); Q's loads are in flight while the walk is
+    // set up.
+    Walk w, w0;   // w0: the walk as it starts (for the safe pass)
+    int first64 = 0;
+    if (!DENSE) {
+        const int64_t row = (a.per_head ? (int64_t)bh * a.nqb : 0) + qt;
+        if (a.kv_cnt != nullptr) {
+            w.cnt = ranked ? ranked_count : a.kv_cnt[row];
+            w.idx = a.kv_idx + row * a.nkb;
+        } else {   // token mode without a list: every key tile
+            w.cnt = a.nkb;
+            w.idx = nullptr;
+        }
+        first64 = lane < w.cnt ? (w.idx != nullptr ? w.idx[lane] : lane) : -1;
+    }
     WaveState<D> st;
     const __bf16* qp = a.q + b * a.sq_b + h * a.sq_h + tok * a.sq_t;
 #pragma unroll
@@ -745,7 +778,6 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
 
     // ---- the walk, in table builds of up to kTableCap chunks (the first one
     // before the accumulators are live)
-    Walk w, w0;   // w0: the walk as it starts (for the safe pass)
     __shared__ int table_n;
     int nch;
     bool first_loaded = false;   // the first chunk's loads already issued
@@ -757,28 +789,16 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
         nch = (w.cend + 31) >> 5;
         w0 = w;
     } else {
-        const LaneGeom lg = lane_geom(a.g, lane);
-        const int64_t row = (a.per_head ? (int64_t)bh * a.nqb : 0) + qt;
-        if (a.kv_cnt != nullptr) {
-            w.cnt = a.kv_cnt[row];
-            w.idx = a.kv_idx + row * a.nkb;
-        } else {   // token mode without a list: every key tile
-            w.cnt = a.nkb;
-            w.idx = nullptr;
-        }
         // leading run of tiles 0,1,2,...: whole scales kept from the start form
         // one contiguous token range
-        int p = 0, first64 = 0;
-        for (;;) {
-            const int v = (p + lane < w.cnt) ? (w.idx != nullptr ? w.idx[p + lane] : p + lane) : -1;
-            if (p == 0) first64 = v;
-            const uint64_t off = __ballot(v != p + lane);
-            if (off) {
-                p += __builtin_ctzll(off);
-                break;
-            }
+        int p = 0;
+        uint64_t off = __ballot(first64 != lane);
+        while (!off) {   // runs past 64 entries (the loads of later entries are waited for in here)
             p += 64;
+            const int v = (p + lane < w.cnt) ? (w.idx != nullptr ? w.idx[p + lane] : p + lane) : -1;
+            off = __ballot(v != p + lane);
         }
+        p += __builtin_ctzll(off);
         // scales wholly inside the run: those whose tiles all precede tile p
         int s = __popcll(__ballot(lane >= 1 && lane <= a.g.n_scales && lg.tb <= p));
         if (TOKEN) s = min(s, a.n_sink);   // only sink scales skip the token test
@@ -1105,7 +1125,8 @@ __global__ __launch_bounds__(256, 2) void attn_pair_bf16_kernel(const AttnArgs a
     const int work = xcd_remap(blockIdx.x, gridDim.x);
     __shared__ __attribute__((aligned(16))) int rank_keys[4][64];
     int bh, pr;
-    work_tile<true>(a, work, npair, lane, rank_keys[wave], bh, pr);   // pairs with the longest lists first
+    int unused_count;
+    work_tile<true>(a, work, npair, lane, rank_keys[wave], bh, pr, unused_count);   // longest lists first
     bh = __builtin_amdgcn_readfirstlane(bh);
     pr = __builtin_amdgcn_readfirstlane(pr);
     const int b = bh / a.H, h = bh - b * a.H;
