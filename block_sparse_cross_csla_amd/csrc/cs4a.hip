@@ -35,6 +35,46 @@ struct ScoreChunk {
     int32_t shape;      // rows | cols << 4
 };
 
+// Maximum of this lane's 16 scores of a chunk (a pairwise tree: fmax is
+// exact, so the order only shortens the dependency chain).
+__device__ __forceinline__ float chunk_max(const f32x16& s) {
+    float m[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = fmaxf(s[i], s[i + 8]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[i], m[i + 4]);
+    return fmaxf(fmaxf(m[0], m[2]), fmaxf(m[1], m[3]));
+}
+
+// Sum of exp2(s c - m) over this lane's 16 scores of a chunk, in a fixed
+// pairwise order.
+__device__ __forceinline__ float chunk_sumexp(const f32x16& s, float c, float m) {
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = p[2 * i] + p[2 * i + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = p[2 * i] + p[2 * i + 1];
+    return (p[0] + p[1]) + (p[2] + p[3]);
+}
+
+// Score of one (query tile, key tile): the mean over the tile's 64 queries of
+// acc[q] f[q] (a query's partial sum and its normalising factor), summed by
+// a group of 8 consecutive lanes in a fixed order (8 values per lane, then a
+// butterfly over the group; every lane of the group ends with the total).
+__device__ __forceinline__ float tile_mean64(const float* acc, const float* f, int lane8) {
+#pragma clang fp contract(off)
+    const float4 a0 = *(const float4*)(acc + 8 * lane8), a1 = *(const float4*)(acc + 8 * lane8 + 4);
+    const float4 f0 = *(const float4*)(f + 8 * lane8), f1 = *(const float4*)(f + 8 * lane8 + 4);
+    float x = ((a0.x * f0.x + a0.y * f0.y) + (a0.z * f0.z + a0.w * f0.w)) +
+              ((a1.x * f1.x + a1.y * f1.y) + (a1.z * f1.z + a1.w * f1.w));
+    x += __shfl_xor(x, 1, 8);
+    x += __shfl_xor(x, 2, 8);
+    x += __shfl_xor(x, 4, 8);
+    return x * (1.0f / 64.0f);
+}
+
 // Eight waves per decision query tile: wave w takes query rows
 // 4 (w & 1) .. 4 (w & 1) + 3 (32 queries) and the key tiles of part w >> 1
 // (tiles part, part + 4, ...).  The chunk table (every key tile split in
@@ -66,7 +106,8 @@ __global__ __launch_bounds__(kScoreThreads) void cs4a_score_kernel(const ScoreAr
     ScoreChunk* table = (ScoreChunk*)(dyn + kScoreParts * NST * STAGE);   // [part][tpp]
     int* halves = (int*)(table + kScoreParts * tpp);                         // [nkb]
     int* nchunks = halves + a.nkb;                                 // [part]
-    float* mrow = (float*)(nchunks + kScoreParts);                 // [part][64]
+    // 16-byte aligned from here on: the tile sums read acc and mrow as float4
+    float* mrow = (float*)(dyn + ((((char*)(nchunks + kScoreParts) - dyn) + 15) & ~15));   // [part][64]
     float* lrow = mrow + 64 * kScoreParts;                         // [part][64]
     float* acc = lrow + 64 * kScoreParts;                                       // [nkb][64 queries]
 
@@ -168,9 +209,7 @@ __global__ __launch_bounds__(kScoreThreads) void cs4a_score_kernel(const ScoreAr
                     if (!(r < cr && col < ccn)) sacc[i] = -INFINITY;
                 }
             }
-            float mx = sacc[0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+            float mx = chunk_max(sacc);
             {
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
                 mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -185,17 +224,16 @@ __global__ __launch_bounds__(kScoreThreads) void cs4a_score_kernel(const ScoreAr
                     m_run = cand;
                 }
             }
-            float part = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) part += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], cl, -m_run));
+            float part = chunk_sumexp(sacc, cl, m_run);
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
             part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);   // both halves of the query's keys
             if (g == 0) acc[ct * 64 + q] += part;
         }
     }
 
-    // merge the parts: common max M, total l, then normalise
-    float l_mine = 0.0f;
+    // merge the parts: common max M, total l, then each (part, query)'s
+    // normalising factor
+    float l_mine = 0.0f, fq = 0.0f;
     if (g == 0)
         for (int kt = par; kt < nkb; kt += kScoreParts) l_mine += acc[kt * 64 + q];
     if (g == 0) {
@@ -213,15 +251,15 @@ __global__ __launch_bounds__(kScoreThreads) void cs4a_score_kernel(const ScoreAr
             const float mp = mrow[p * 64 + q];
             if (mp != -INFINITY) l_q += lrow[p * 64 + q] * __builtin_amdgcn_exp2f(mp - M);
         }
-        const float f = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M) / l_q;
-        for (int kt = par; kt < nkb; kt += kScoreParts) acc[kt * 64 + q] *= f;
+        fq = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M) / l_q;
     }
+    __syncthreads();   // every part's maximum and sum read
+    if (g == 0) mrow[par * 64 + q] = fq;   // now: the normalising factor of (part, query)
     __syncthreads();
     float* out = a.scores + ((int64_t)bh * a.nqb + qt) * nkb;
-    for (int kt = tid; kt < nkb; kt += kScoreThreads) {
-        float sum = 0.0f;
-        for (int qq = 0; qq < 64; ++qq) sum += acc[kt * 64 + qq];
-        out[kt] = sum * (1.0f / 64.0f);
+    for (int kt = tid >> 3; kt < nkb; kt += kScoreThreads / 8) {
+        const float v = tile_mean64(acc + kt * 64, mrow + (kt % kScoreParts) * 64, tid & 7);
+        if ((tid & 7) == 0) out[kt] = v;
     }
 }
 
@@ -252,7 +290,8 @@ __global__ __launch_bounds__(kScore2Threads) void cs4a_score2_kernel(const Score
     ScoreChunk* table = (ScoreChunk*)(dyn + kScoreParts * NST * STAGE);   // [part][tpp]
     int* halves = (int*)(table + kScoreParts * tpp);                         // [nkb]
     int* nchunks = halves + a.nkb;                                 // [part]
-    float* mrow = (float*)(nchunks + kScoreParts);                 // [part][NQ]
+    // 16-byte aligned from here on: the tile sums read acc and mrow as float4
+    float* mrow = (float*)(dyn + ((((char*)(nchunks + kScoreParts) - dyn) + 15) & ~15));   // [part][NQ]
     float* lrow = mrow + NQ * kScoreParts;                         // [part][NQ]
     float* acc = lrow + NQ * kScoreParts;                          // [nkb][NQ]
 
@@ -359,9 +398,7 @@ __global__ __launch_bounds__(kScore2Threads) void cs4a_score2_kernel(const Score
                     if (!(r < cr && col < ccn)) sacc[i] = -INFINITY;
                 }
             }
-            float mx = sacc[0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+            float mx = chunk_max(sacc);
             {
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
                 mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -376,17 +413,16 @@ __global__ __launch_bounds__(kScore2Threads) void cs4a_score2_kernel(const Score
                     m_run = cand;
                 }
             }
-            float part = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) part += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], cl, -m_run));
+            float part = chunk_sumexp(sacc, cl, m_run);
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
             part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
             if (g == 0) acc[ct * NQ + q] += part;
         }
     }
 
-    // merge the parts: common max M, total l, then normalise
-    float l_mine = 0.0f;
+    // merge the parts: common max M, total l, then each (part, query)'s
+    // normalising factor
+    float l_mine = 0.0f, fq = 0.0f;
     if (g == 0)
         for (int kt = par; kt < nkb; kt += kScoreParts) l_mine += acc[kt * NQ + q];
     if (g == 0) {
@@ -404,16 +440,16 @@ __global__ __launch_bounds__(kScore2Threads) void cs4a_score2_kernel(const Score
             const float mp = mrow[p * NQ + q];
             if (mp != -INFINITY) l_q += lrow[p * NQ + q] * __builtin_amdgcn_exp2f(mp - M);
         }
-        const float f = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M) / l_q;
-        for (int kt = par; kt < nkb; kt += kScoreParts) acc[kt * NQ + q] *= f;
+        fq = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - M) / l_q;
     }
+    __syncthreads();   // every part's maximum and sum read
+    if (g == 0) mrow[par * NQ + q] = fq;   // now: the normalising factor of (part, query)
     __syncthreads();
-    for (int e = tid; e < kScore2Tiles * nkb; e += kScore2Threads) {
+    for (int e = tid >> 3; e < kScore2Tiles * nkb; e += kScore2Threads / 8) {
         const int t2 = e / nkb, kt = e - t2 * nkb;
-        if (2 * tp + t2 >= a.nqb) continue;
-        float sum = 0.0f;
-        for (int qq = 0; qq < 64; ++qq) sum += acc[kt * NQ + t2 * 64 + qq];
-        a.scores[((int64_t)bh * a.nqb + 2 * tp + t2) * nkb + kt] = sum * (1.0f / 64.0f);
+        if (2 * tp + t2 >= a.nqb) continue;   // the same for the 8 lanes of a group
+        const float v = tile_mean64(acc + kt * NQ + t2 * 64, mrow + (kt % kScoreParts) * NQ + t2 * 64, tid & 7);
+        if ((tid & 7) == 0) a.scores[((int64_t)bh * a.nqb + 2 * tp + t2) * nkb + kt] = v;
     }
 }
 
@@ -571,8 +607,8 @@ namespace {
 
 size_t score_shmem(int parts, int stages, int head_dim, int nkb, int nq) {
     return (size_t)parts * stages * 32 * head_dim * 2 + parts * (size_t)(nkb / 2 + 2) * sizeof(ScoreChunk) +
-           (size_t)(nkb + parts) * sizeof(int) + 2 * (size_t)nq * parts * sizeof(float) +
-           (size_t)nkb * nq * sizeof(float);
+           (size_t)(nkb + parts) * sizeof(int) + 12 + 2 * (size_t)nq * parts * sizeof(float) +
+           (size_t)nkb * nq * sizeof(float);   // 12: padding to the 16-byte aligned float arrays
 }
 
 template <typename K>
