@@ -115,20 +115,9 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
     else wait_vm<0>();   // anything else: wait for everything
 }
 
-// Wait until at most N vector-memory operations and no LDS operation of this
-// wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
-}
-
 // Wait for every outstanding vector-memory and LDS operation of this wave.
 __device__ __forceinline__ void wait_all() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(size_t)((const __attribute__((address_space(3))) char*)p);
 }
 
 }  // namespace vs
