@@ -968,6 +968,187 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     }
 }
 
+// ---- dense attention over few query blocks: each block's keys split over P wave pairs
+//
+// A dense launch over a handful of 64-query blocks (the small scales of a
+// generation step, the decision scale) leaves most of the chip idle while
+// every block walks all its keys in turn.  Here one workgroup = one 64-query
+// block and P wave pairs: pair p walks the p-th of P contiguous ranges of
+// 32-key chunks with the chunk step of attn_fwd_bf16_kernel (its own two LDS
+// stages, its own running maximum, the exact first chunk and the exact redo
+// of a walk that overflowed), and the pairs' maxima, row sums and O^T are
+// merged through LDS at the end: the same softmax in arithmetic, summed in
+// another order.  All pairs pass the same number of workgroup barriers (a
+// pair with one chunk fewer passes an extra one).
+template <int D, int P>
+__global__ __launch_bounds__(128 * P, P == 2 ? 2 : 1) void attn_dense_split_kernel(const AttnArgs a) {
+    constexpr int KSTEPS = D / 16;
+    constexpr int MBLK = D / 32;
+    constexpr int STAGE = 32 * D * 2;
+    extern __shared__ __attribute__((aligned(1024))) char dyn[];   // [P][stage][K, V]; then the merge
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int part = wave >> 1, pw = wave & 1;   // wave pair, and wave within it
+    const int n = lane & 31, g = lane >> 5;
+    const int64_t nqt = (a.nq + 63) / 64;
+    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = (int)(work / nqt);
+    const int64_t qt = work - (int64_t)bh * nqt;
+    const int b = bh / a.H, h = bh - b * a.H;
+    // this lane's query (clamped for the tail block; recomputed for the epilogue
+    // rather than kept live across the walk)
+    auto query_tok = [&]() { return min(64 * qt + 32 * pw + n, a.nq - 1); };
+    const __bf16* kh = a.k + b * a.sk_b + h * a.sk_h;
+    const __bf16* vh = a.v + b * a.sv_b + h * a.sv_h;
+    const int32_t krb = (int32_t)(a.sk_t * 2), vrb = (int32_t)(a.sv_t * 2);
+    const float c = a.scale_log2;
+    const lds_ptr L = (lds_ptr)(dyn + part * 4 * STAGE);   // this pair's stages (loads)
+
+    WaveState<D> st;
+    const __bf16* qp = a.q + b * a.sq_b + h * a.sq_h + query_tok() * a.sq_t;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) st.qreg[s] = *(const bf16x8*)(qp + 16 * s + 8 * g);
+    init_lds_offsets<D>(st, lane);
+    {   // the pair's stages: its offset goes into the per-lane operand offsets, so
+        // that the stage constants stay in the LDS reads' immediate offsets
+        const uint32_t part_off = (uint32_t)(part * 4 * STAGE);
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) st.koff[s] += part_off;
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb) st.voff[mb][0] += part_off, st.voff[mb][1] += part_off;
+    }
+    LoadPlan<D> plan;
+    make_plan<D>(plan, pw, lane, a.sk_t, a.sv_t);
+
+    // this pair's chunks [c0, c0 + nch); nmax barriers' worth for every pair
+    const int nch_all = (int)((a.nk + 31) >> 5);
+    const int c0 = (int)((int64_t)nch_all * part / P);
+    const int nch = (int)((int64_t)nch_all * (part + 1) / P) - c0;
+    const int nmax = (nch_all + P - 1) / P;
+    auto desc = [&](int ci) -> Chunk {
+        const int base = 32 * (c0 + ci);
+        return unpack_chunk(base, pack_info(8, 4, 8, (int)min((int64_t)32, a.nk - base)));
+    };
+
+    __shared__ int bad_any;
+    auto walk = [&](auto exact_tag) {
+        constexpr bool EXACT = decltype(exact_tag)::value;
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] = (f32x16)0.0f;
+        st.m_run = -1e30f;   // finite: a fully masked chunk gives P = 0, not NaN
+        st.l_run = 0.0f;
+        PipeState<D> ps;
+        pipe_reset<D>(ps);
+        Chunk cur = desc(0), nxt;
+        if (nch > 0) load_chunk<D>(plan, kh, vh, krb, vrb, cur, L, L + STAGE, pw, lane);
+        auto step = [&](auto stage_tag, auto ex_tag, int ci) {
+            constexpr int S = decltype(stage_tag)::value ? 1 : 0;
+            wait_all();
+            wg_barrier();
+            if (ci + 1 < nch) {
+                nxt = desc(ci + 1);
+                load_chunk<D>(plan, kh, vh, krb, vrb, nxt, L + 2 * (1 - S) * STAGE, L + (3 - 2 * S) * STAGE, pw,
+                              lane);
+            }
+            pipe_chunk<D, decltype(ex_tag)::value>(st, ps, dyn + 2 * S * STAGE, dyn + (2 * S + 1) * STAGE, cur, c,
+                                                   lane, 0xffffu);
+            cur = nxt;
+        };
+        int ci0 = 0;
+        if (!EXACT && nch > 0) {   // the walk's first two chunks: the first exact
+            step(IntC<false>{}, IntC<true>{}, 0);
+            if (nch > 1) step(IntC<true>{}, IntC<false>{}, 1);
+            ci0 = 2;
+        }
+        int ci = ci0;
+        for (; ci + 1 < nch; ci += 2) {
+            step(IntC<false>{}, IntC<EXACT>{}, ci);
+            step(IntC<true>{}, IntC<EXACT>{}, ci + 1);
+        }
+        if (ci < nch) step(IntC<false>{}, IntC<EXACT>{}, ci);
+        pipe_drain<D>(st, ps);
+        for (int k = max(nch, 0); k < nmax; ++k) {   // the barriers of the longer pairs' last steps
+            wait_all();
+            wg_barrier();
+        }
+        bool bad = !(__builtin_fabsf(st.l_run) <= 3.0e38f) || (nch > 0 && half_swap_sum(st.l_run) == 0.0f);
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) bad |= !(__builtin_fabsf(st.oacc[mb][i]) <= 3.0e38f);
+        return bad;
+    };
+    {
+        if (threadIdx.x == 0) bad_any = 0;
+        __syncthreads();
+        const bool wbad = __builtin_amdgcn_ballot_w64(walk(IntC<false>{})) != 0;
+        if (wbad && lane == 0) bad_any = 1;   // every writer stores the same value
+        __syncthreads();   // every pair done with its stages; the flag is visible
+        if (bad_any) {
+            walk(IntC<true>{});
+            __syncthreads();
+        }
+    }
+
+    // ---- merge the pairs into pair 0 (same lane layout in every pair)
+    float* mbuf = (float*)dyn;              // [P][2][64] running maxima
+    float* lbuf = mbuf + P * 128;           // [P][2][64] row-sum halves
+    float* obuf = lbuf + P * 128;           // [P - 1][2][MBLK * 16][64] O^T
+    const int slot = (part * 2 + pw) * 64 + lane;
+    if (part > 0) {
+        mbuf[slot] = st.m_run;
+        lbuf[slot] = st.l_run;
+        float* ob = obuf + (((part - 1) * 2 + pw) * MBLK * 16) * 64 + lane;
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ob[(mb * 16 + i) * 64] = st.oacc[mb][i];
+    }
+    __syncthreads();
+    if (part != 0) return;
+    float M = st.m_run;
+#pragma unroll
+    for (int p = 1; p < P; ++p) M = fmaxf(M, mbuf[(p * 2 + pw) * 64 + lane]);
+    {
+        const float s0 = __builtin_amdgcn_exp2f(st.m_run - M);
+        st.l_run *= s0;
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb) st.oacc[mb] *= s0;
+    }
+#pragma unroll
+    for (int p = 1; p < P; ++p) {
+        const float sp = __builtin_amdgcn_exp2f(mbuf[(p * 2 + pw) * 64 + lane] - M);
+        st.l_run += lbuf[(p * 2 + pw) * 64 + lane] * sp;
+        const float* ob = obuf + (((p - 1) * 2 + pw) * MBLK * 16) * 64 + lane;
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st.oacc[mb][i] += ob[(mb * 16 + i) * 64] * sp;
+    }
+    st.m_run = M;
+
+    // ---- epilogue (as attn_fwd_bf16_kernel's)
+    const float l_tot = half_swap_sum(st.l_run);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const int64_t tok = query_tok();
+    if (64 * qt + 32 * pw + n < a.nq) {
+        __bf16* op = a.o + b * a.so_b + h * a.so_h + tok * a.so_t;
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x4 val;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) val[e] = (__bf16)(st.oacc[mb][4 * kk + e] * inv);
+                *(bf16x4*)(op + 32 * mb + 8 * kk + 4 * g) = val;
+            }
+        }
+        if (a.lse != nullptr && g == 0)
+            a.lse[(int64_t)bh * a.nq + tok] =
+                l_tot > 0.0f ? (st.m_run + __builtin_log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+    }
+}
+
 // ---- 128-query workgroups over pairs of query tiles (the block-128 variant)
 //
 // One workgroup = four waves = query tiles 2p and 2p + 1 of one (b, h)
@@ -1293,11 +1474,41 @@ hipError_t launch_attn_pair_bf16(const AttnArgs& a, int head_dim, hipStream_t st
     return hipGetLastError();
 }
 
+namespace {
+
+template <typename K>
+hipError_t launch_dense_split(K kernel, int64_t blocks, int parts, size_t shmem, const AttnArgs& a,
+                              hipStream_t stream) {
+    const hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(128 * parts), shmem, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStream_t stream) {
     const int64_t nqt = dense ? (a.nq + 63) / 64 : a.nqb;
     const int64_t blocks = nqt * a.B * a.H;
     dim3 grid((unsigned)blocks), block(128);
     const bool token = a.token != 0 && !dense;
+    if (dense) {
+        // few query blocks: split each block's keys over wave pairs so that the
+        // launch still fills the chip in one round (4 pairs: 128 KB of LDS, one
+        // workgroup per CU; 2 pairs: two per CU), each pair walking >= 2 chunks
+        const int64_t nch_all = (a.nk + 31) >> 5;
+        const size_t stage = (size_t)32 * head_dim * 2;
+        if (blocks <= 256 && nch_all >= 8) {
+            if (head_dim == 128)
+                return launch_dense_split(attn_dense_split_kernel<128, 4>, blocks, 4, 4 * 4 * stage, a, stream);
+            return launch_dense_split(attn_dense_split_kernel<64, 4>, blocks, 4, 4 * 4 * stage, a, stream);
+        }
+        if (blocks <= 512 && nch_all >= 4) {
+            if (head_dim == 128)
+                return launch_dense_split(attn_dense_split_kernel<128, 2>, blocks, 2, 2 * 4 * stage, a, stream);
+            return launch_dense_split(attn_dense_split_kernel<64, 2>, blocks, 2, 2 * 4 * stage, a, stream);
+        }
+    }
     if (head_dim == 128) {
         if (dense) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true, false>), grid, block, 0, stream, a);
         else if (token) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false, true>), grid, block, 0, stream, a);

@@ -129,6 +129,29 @@ def test_bf16_dense(nq, nk, d):
     _compare(o, lse, ro, rl, BF16_TOL, f"dense {nq}x{nk} d={d}")
 
 
+@pytest.mark.parametrize("B,H,nq,nk,d,spike", [(1, 8, 2560, 700, 64, 0.0), (2, 16, 576, 1497, 128, 0.0),
+                                                (1, 2, 300, 1000, 128, 8.0), (1, 8, 2560, 700, 64, 48.0)])
+def test_bf16_dense_split_walks(B, H, nq, nk, d, spike):
+    """Dense launches over few 64-query blocks walk each block's keys in 2 or 4
+    contiguous ranges, one per wave pair, and merge the pairs (the grid sizes
+    here take 2, 2, 4 and 2 pairs).  A spike scales a few keys in the last
+    range: by 8 the pair's running maximum is raised within its walk and sits
+    far above the other pairs' at the merge; by 48 the pair's fast walk
+    overflows and the workgroup redoes its walks in the exact form."""
+    vs = _vs()
+    q, k, v = gaussian(7, 71, B, H, nq, nk, d)
+    if spike:
+        rows = np.arange(nk * 7 // 8, nk * 7 // 8 + 5)
+        k[:, :, rows] = round_bf16(k[:, :, rows] * spike)
+    o, lse = vs.dense_attn_fwd(to_device(q), to_device(k), to_device(v))
+    torch.cuda.synchronize()
+    bh = [(0, 0), (B - 1, H - 1), (0, H // 2)]
+    rows = [0, 1, 63, 64, 65, nq // 2, nq - 1]
+    ro, rl = OA.dense_attention(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), 1 / math.sqrt(d),
+                                q_rows=rows, bh=bh)
+    _compare(o, lse, ro, rl, BF16_TOL, f"dense split {B}x{H}x{nq}x{nk} d={d} spike={spike}")
+
+
 @pytest.mark.parametrize("nq,nk,d", [(100, 333, 64), (64, 64, 128)])
 def test_fp32_dense(nq, nk, d):
     vs = _vs()
