@@ -1495,15 +1495,16 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStre
     if (dense) {
         // few query blocks: split each block's keys over wave pairs so that the
         // launch still fills the chip in one round (4 pairs: 128 KB of LDS, one
-        // workgroup per CU; 2 pairs: two per CU), each pair walking >= 2 chunks
+        // workgroup per CU; 2 pairs: two per CU), each pair walking >= 6 chunks
+        // (shorter walks lose more to the merge than they gain)
         const int64_t nch_all = (a.nk + 31) >> 5;
         const size_t stage = (size_t)32 * head_dim * 2;
-        if (blocks <= 256 && nch_all >= 8) {
+        if (blocks <= 256 && nch_all >= 24) {
             if (head_dim == 128)
                 return launch_dense_split(attn_dense_split_kernel<128, 4>, blocks, 4, 4 * 4 * stage, a, stream);
             return launch_dense_split(attn_dense_split_kernel<64, 4>, blocks, 4, 4 * 4 * stage, a, stream);
         }
-        if (blocks <= 512 && nch_all >= 4) {
+        if (blocks <= 512 && nch_all >= 12) {
             if (head_dim == 128)
                 return launch_dense_split(attn_dense_split_kernel<128, 2>, blocks, 2, 2 * 4 * stage, a, stream);
             return launch_dense_split(attn_dense_split_kernel<64, 2>, blocks, 2, 2 * 4 * stage, a, stream);

@@ -274,9 +274,9 @@ int varsparse_attn_fwd_token(const varsparse_geom* geom, int32_t q_scale, int32_
  * kernel vs dense FlashAttention on the last scale).  Every query attends to
  * all nk keys.  Layouts and lse as for varsparse_attn_fwd; nq, nk >= 1.
  * bf16 or fp32, head_dim in {64, 128}.  A bf16 launch of at most 512 blocks of
- * 64 queries (B * H * ceil(nq / 64)) splits each block's keys over 2 or 4 wave
- * groups and merges their partial softmaxes: the same result up to rounding
- * order.
+ * 64 queries (B * H * ceil(nq / 64)) over at least 384 keys splits each block's
+ * keys over 2 or 4 wave groups and merges their partial softmaxes: the same
+ * result up to rounding order.
  */
 int varsparse_dense_attn_fwd(varsparse_dtype dtype, int32_t B, int32_t H, int32_t head_dim,
                              int64_t nq, int64_t nk,

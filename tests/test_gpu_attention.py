@@ -130,11 +130,12 @@ def test_bf16_dense(nq, nk, d):
 
 
 @pytest.mark.parametrize("B,H,nq,nk,d,spike", [(1, 8, 2560, 700, 64, 0.0), (2, 16, 576, 1497, 128, 0.0),
-                                                (1, 2, 300, 1000, 128, 8.0), (1, 8, 2560, 700, 64, 48.0)])
+                                                (1, 2, 300, 1000, 128, 8.0), (1, 8, 2560, 700, 64, 48.0),
+                                                (1, 2, 130, 1000, 64, 8.0)])
 def test_bf16_dense_split_walks(B, H, nq, nk, d, spike):
     """Dense launches over few 64-query blocks walk each block's keys in 2 or 4
     contiguous ranges, one per wave pair, and merge the pairs (the grid sizes
-    here take 2, 2, 4 and 2 pairs).  A spike scales a few keys in the last
+    here take 2, 2, 4, 2 and 4 pairs).  A spike scales a few keys in the last
     range: by 8 the pair's running maximum is raised within its walk and sits
     far above the other pairs' at the merge; by 48 the pair's fast walk
     overflows and the workgroup redoes its walks in the exact form."""
