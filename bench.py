@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0
 # over GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), recorded with the SHA-256 of the
 # kernel sources they were taken on; reported only while those sources are
 # unchanged.
-TRAFFIC = {"bytes": 439.4e6, "mfma_busy": 0.361, "sources_sha256": "ba006d216437868ef69510371fdb8f5dca05159b11b92f840590b4dd36a0ee5a"}
+TRAFFIC = {"bytes": 431.7e6, "mfma_busy": 0.359, "sources_sha256": "ba006d216437868ef69510371fdb8f5dca05159b11b92f840590b4dd36a0ee5a"}
 KERNEL_SOURCES = ("block_sparse_cross_csla_amd/csrc/attn_bf16.hip", "block_sparse_cross_csla_amd/csrc/common.h",
                   "block_sparse_cross_csla_amd/csrc/kernel_args.h")
 
