@@ -37,6 +37,22 @@ def test_scores_match_membership_matmul_route():
     assert np.abs(sc.sum(axis=-1) - 1).max() < 1e-12
 
 
+def test_scores_each_query_normalised_by_its_own_maximum():
+    """Every query's softmax over the keys sums to 1 whatever the other
+    queries' score ranges: with one query's scores ~2000 above another's, a
+    maximum shared across queries would underflow the lower query's weights
+    to zero (and its normalisation to 0/0)."""
+    sides, D, t = (1, 2, 4), 2, 2
+    nk = 1 + 4 + 16
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 16, 8))
+    k = rng.standard_normal((1, 1, nk, 8))
+    q[0, 0, 3] = 4000.0 * k[0, 0, 7] / np.dot(k[0, 0, 7], k[0, 0, 7])   # query 3 scores key 7 at 4000
+    sc = cs4a.block_scores(q, k, sides, D, t, 0.5)
+    assert np.isfinite(sc).all()
+    np.testing.assert_allclose(sc.sum(axis=-1), 1.0, rtol=0, atol=1e-12)
+
+
 def test_top_p_hand_fixture():
     fx = json.load(open(GOLDEN))["top_p"]
     for case in fx["cases"]:
@@ -200,6 +216,13 @@ def test_top_k_count():
     assert OC.top_k_count(5, 0.0001) == 1            # at least one tile
     assert OC.top_k_count(5, 0.0) == 1               # even for a zero fraction
     assert OC.top_k_count(5, 1.0) == 5
+    # the product is taken in float32 (the precision of the fraction), not in
+    # double: float32(0.07) * 100 = 7.0000000298 rounds to 7.0 in float32 -> 7,
+    # while 0.07 * 100 in double is 7.000000000000001 -> 8; float32(0.09) * 300
+    # = 27.00000107 rounds up to 27.0000019 (27 + 2^-19) in float32 -> 28,
+    # while 0.09 * 300 in double is exactly 27 -> 27
+    assert OC.top_k_count(100, 0.07) == 7
+    assert OC.top_k_count(300, 0.09) == 28
 
 
 def test_top_k_full_fraction_keeps_all_and_argmax():
