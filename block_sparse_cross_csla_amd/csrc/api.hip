@@ -123,16 +123,18 @@ int map_indices_impl(const varsparse_geom* geom, int32_t d_scale, int32_t n_targ
     if (n_targets < 1 || n_targets > vs::kMaxTargets || t_scales == nullptr) return VARSPARSE_EINVAL;
     if (kv_cnt == nullptr || kv_idx == nullptr) return VARSPARSE_EINVAL;
     if (d_scale < 0 || d_scale >= geom->n_scales || geom->side[d_scale] % geom->tile != 0) return VARSPARSE_EINVAL;
+    if (B < 0 || H < 0) return VARSPARSE_EINVAL;
+    const bool empty = B == 0 || H == 0;
     int t_max = d_scale;
     for (int i = 0; i < n_targets; ++i) {
         const int T = t_scales[i];
         if (T < d_scale || T >= geom->n_scales || geom->side[T] % geom->tile != 0) return VARSPARSE_EINVAL;
-        if (kv_cnt[i] == nullptr || kv_idx[i] == nullptr) return VARSPARSE_EINVAL;
+        if (!empty && (kv_cnt[i] == nullptr || kv_idx[i] == nullptr)) return VARSPARSE_EINVAL;
         t_max = std::max(t_max, T);
     }
     if (n_sink < 0 || n_sink > d_scale) return VARSPARSE_EINVAL;
     if (!(top_p > 0.0f && top_p <= 1.0f)) return VARSPARSE_EINVAL;
-    if (B < 1 || H < 1) return VARSPARSE_EINVAL;
+    if (empty) return VARSPARSE_OK;   // empty batch: nothing to compute
     if (scores == nullptr) return VARSPARSE_EINVAL;
     if ((sel_cnt == nullptr) != (sel_idx == nullptr)) return VARSPARSE_EINVAL;
     const vs::DevGeom gD = vs::make_dev_geom(*geom, d_scale);
@@ -241,15 +243,16 @@ int varsparse_attn_fwd(const varsparse_geom* geom, int32_t q_scale, varsparse_dt
     if (q_scale < 0 || q_scale >= geom->n_scales) return VARSPARSE_EINVAL;
     if (geom->side[q_scale] % geom->tile != 0) return VARSPARSE_EINVAL;
     if (dtype != VARSPARSE_BF16 && dtype != VARSPARSE_FP32) return VARSPARSE_EINVAL;
-    if (B < 1 || H < 1) return VARSPARSE_EINVAL;
-    if (!q || !k || !v || !o || !strides || !kv_cnt || !kv_idx) return VARSPARSE_EINVAL;
+    if (B < 0 || H < 0) return VARSPARSE_EINVAL;
     if (lists_per_head != 0 && lists_per_head != 1) return VARSPARSE_EINVAL;
     if (!scale_ok(softmax_scale)) return VARSPARSE_EINVAL;
     if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VARSPARSE_EINVAL;
-    if (!strides_ok(strides, 12, dtype == VARSPARSE_BF16 ? 8 : 4)) return VARSPARSE_EINVAL;
     if (dtype == VARSPARSE_BF16 && geom->tile != 8) return VARSPARSE_EUNSUPPORTED;
     if (dtype == VARSPARSE_FP32 && geom->tile * geom->tile > 64) return VARSPARSE_EUNSUPPORTED;
+    if (B == 0 || H == 0) return VARSPARSE_OK;   // empty batch: nothing to compute
+    if (!q || !k || !v || !o || !strides || !kv_cnt || !kv_idx) return VARSPARSE_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VARSPARSE_EINVAL;
+    if (!strides_ok(strides, 12, dtype == VARSPARSE_BF16 ? 8 : 4)) return VARSPARSE_EINVAL;
     const vs::DevGeom g = vs::make_dev_geom(*geom, q_scale);
     const int nqb = g.nb[q_scale] * g.nb[q_scale];
     if ((int64_t)nqb * B * H > 0x7fffffff) return VARSPARSE_EINVAL;
@@ -287,14 +290,15 @@ int varsparse_attn_fwd_pair(const varsparse_geom* geom, int32_t q_scale, int32_t
     if (rc) return rc;
     if (q_scale < 0 || q_scale >= geom->n_scales) return VARSPARSE_EINVAL;
     if (geom->side[q_scale] % geom->tile != 0) return VARSPARSE_EINVAL;
-    if (B < 1 || H < 1) return VARSPARSE_EINVAL;
-    if (!q || !k || !v || !o || !strides || !kv_cnt || !kv_idx) return VARSPARSE_EINVAL;
+    if (B < 0 || H < 0) return VARSPARSE_EINVAL;
     if (lists_per_head != 0 && lists_per_head != 1) return VARSPARSE_EINVAL;
     if (!scale_ok(softmax_scale)) return VARSPARSE_EINVAL;
     if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;
+    if (geom->tile != 8) return VARSPARSE_EUNSUPPORTED;
+    if (B == 0 || H == 0) return VARSPARSE_OK;   // empty batch: nothing to compute
+    if (!q || !k || !v || !o || !strides || !kv_cnt || !kv_idx) return VARSPARSE_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VARSPARSE_EINVAL;
     if (!strides_ok(strides, 12, 8)) return VARSPARSE_EINVAL;
-    if (geom->tile != 8) return VARSPARSE_EUNSUPPORTED;
     const vs::DevGeom g = vs::make_dev_geom(*geom, q_scale);
     const int nqb = g.nb[q_scale] * g.nb[q_scale];
     if ((int64_t)((nqb + 1) / 2) * B * H > 0x7fffffff) return VARSPARSE_EINVAL;
@@ -323,15 +327,16 @@ int varsparse_attn_fwd_token(const varsparse_geom* geom, int32_t q_scale, int32_
     if (geom->side[q_scale] % geom->tile != 0) return VARSPARSE_EINVAL;
     if (n_sink < 0 || n_sink > q_scale || radius == nullptr) return VARSPARSE_EINVAL;
     if (geom->side[q_scale] > 4096) return VARSPARSE_EUNSUPPORTED;   // projections use 24-bit exact quotients
-    if (B < 1 || H < 1) return VARSPARSE_EINVAL;
-    if (!q || !k || !v || !o || !strides) return VARSPARSE_EINVAL;
-    if ((kv_cnt == nullptr) != (kv_idx == nullptr)) return VARSPARSE_EINVAL;
+    if (B < 0 || H < 0) return VARSPARSE_EINVAL;
     if (lists_per_head != 0 && lists_per_head != 1) return VARSPARSE_EINVAL;
     if (!scale_ok(softmax_scale)) return VARSPARSE_EINVAL;
     if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;
+    if (geom->tile != 8) return VARSPARSE_EUNSUPPORTED;
+    if (B == 0 || H == 0) return VARSPARSE_OK;   // empty batch: nothing to compute
+    if (!q || !k || !v || !o || !strides) return VARSPARSE_EINVAL;
+    if ((kv_cnt == nullptr) != (kv_idx == nullptr)) return VARSPARSE_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VARSPARSE_EINVAL;
     if (!strides_ok(strides, 12, 8)) return VARSPARSE_EINVAL;
-    if (geom->tile != 8) return VARSPARSE_EUNSUPPORTED;
     const vs::DevGeom g = vs::make_dev_geom(*geom, q_scale);
     const int nqb = g.nb[q_scale] * g.nb[q_scale];
     if ((int64_t)nqb * B * H > 0x7fffffff) return VARSPARSE_EINVAL;
@@ -354,11 +359,12 @@ int varsparse_dense_attn_fwd(varsparse_dtype dtype, int32_t B, int32_t H, int32_
                              const void* q, const void* k, const void* v, void* o, float* lse,
                              const int64_t strides[12], float softmax_scale, void* stream) {
     if (dtype != VARSPARSE_BF16 && dtype != VARSPARSE_FP32) return VARSPARSE_EINVAL;
-    if (B < 1 || H < 1 || nq < 1 || nk < 1) return VARSPARSE_EINVAL;
+    if (B < 0 || H < 0 || nq < 0 || nk < 1) return VARSPARSE_EINVAL;
     if (nk >= ((int64_t)1 << 30)) return VARSPARSE_EUNSUPPORTED;
-    if (!q || !k || !v || !o || !strides) return VARSPARSE_EINVAL;
     if (!scale_ok(softmax_scale)) return VARSPARSE_EINVAL;
     if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;
+    if (B == 0 || H == 0 || nq == 0) return VARSPARSE_OK;   // no queries: nothing to compute
+    if (!q || !k || !v || !o || !strides) return VARSPARSE_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VARSPARSE_EINVAL;
     if (!strides_ok(strides, 12, dtype == VARSPARSE_BF16 ? 8 : 4)) return VARSPARSE_EINVAL;
     if (((nq + 63) / 64) * B * H > 0x7fffffff) return VARSPARSE_EINVAL;
@@ -388,8 +394,9 @@ int varsparse_dense_attn_fwd(varsparse_dtype dtype, int32_t B, int32_t H, int32_
 int varsparse_ocache_correct(int32_t B, int32_t H, int32_t head_dim, int32_t side_d, int32_t side_t,
                              const void* o_full_d, const void* o_sparse_d, void* o_t,
                              const int64_t strides[9], void* stream) {
-    if (B < 1 || H < 1 || side_d < 1 || side_t < side_d || side_t > 65535) return VARSPARSE_EINVAL;
+    if (B < 0 || H < 0 || side_d < 1 || side_t < side_d || side_t > 65535) return VARSPARSE_EINVAL;
     if (head_dim < 8 || head_dim % 8 != 0 || head_dim > 1024) return VARSPARSE_EINVAL;
+    if (B == 0 || H == 0) return VARSPARSE_OK;   // empty batch: nothing to compute
     if (!o_full_d || !o_sparse_d || !o_t || !strides) return VARSPARSE_EINVAL;
     if (!aligned16(o_full_d) || !aligned16(o_sparse_d) || !aligned16(o_t)) return VARSPARSE_EINVAL;
     if (!strides_ok(strides, 9, 8)) return VARSPARSE_EINVAL;
@@ -407,8 +414,9 @@ int varsparse_join_lists(int32_t sets, int32_t rows, int32_t nkb, int32_t join,
                          const int32_t* a_cnt, const int32_t* a_idx, int32_t a_per_set,
                          const int32_t* b_cnt, const int32_t* b_idx, int32_t b_per_set,
                          int32_t* out_cnt, int32_t* out_idx, void* stream) {
-    if (sets < 1 || rows < 1 || nkb < 1 || nkb > 65536) return VARSPARSE_EINVAL;
+    if (sets < 0 || rows < 1 || nkb < 1 || nkb > 65536) return VARSPARSE_EINVAL;
     if (join != VARSPARSE_JOIN_UNION && join != VARSPARSE_JOIN_INTERSECTION) return VARSPARSE_EINVAL;
+    if (sets == 0) return VARSPARSE_OK;   // no list sets: nothing to compute
     if ((int64_t)sets * rows >= ((int64_t)1 << 31)) return VARSPARSE_EINVAL;
     if (!a_cnt || !a_idx || !b_cnt || !b_idx || !out_cnt || !out_idx) return VARSPARSE_EINVAL;
     if (out_cnt == a_cnt || out_cnt == b_cnt || out_idx == a_idx || out_idx == b_idx) return VARSPARSE_EINVAL;

@@ -45,6 +45,12 @@
  * outside what the kernels implement).  Work is enqueued on `stream` (a
  * hipStream_t; NULL = the default stream) and is asynchronous; a launch
  * failure returns VARSPARSE_EHIP.  No C++ exception crosses this interface.
+ *
+ * Empty inputs: B == 0 or H == 0 (varsparse_dense_attn_fwd: also nq == 0;
+ * varsparse_join_lists: sets == 0) is valid.  Once the geometry and the
+ * scalar arguments pass, such a call returns VARSPARSE_OK, enqueues nothing
+ * and reads no data pointer, which may then be NULL.  Negative sizes are
+ * EINVAL.
  */
 #ifndef VARSPARSE_H
 #define VARSPARSE_H
@@ -272,7 +278,7 @@ int varsparse_attn_fwd_token(const varsparse_geom* geom, int32_t q_scale, int32_
  * Dense attention written with the same tile engine, the comparator the
  * pages measure the sparse kernel against ("Main Findings": the block-wise
  * kernel vs dense FlashAttention on the last scale).  Every query attends to
- * all nk keys.  Layouts and lse as for varsparse_attn_fwd; nq, nk >= 1.
+ * all nk keys.  Layouts and lse as for varsparse_attn_fwd; nq >= 0, nk >= 1.
  * bf16 or fp32, head_dim in {64, 128}.  A bf16 launch of at most 512 blocks of
  * 64 queries (B * H * ceil(nq / 64)) over at least 384 keys splits each block's
  * keys over 2 or 4 wave groups and merges their partial softmaxes: the same

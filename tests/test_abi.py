@@ -1,7 +1,7 @@
 """The C ABI without a GPU: the library loads, exports every function the
 header declares, computes counts on the host, and rejects malformed or
-unsupported arguments before touching HIP (every call here fails validation,
-so none of them launches anything)."""
+unsupported arguments before touching HIP.  Every call here either fails
+validation or has an empty batch, so none of them launches anything."""
 import ctypes
 import os
 import re
@@ -97,7 +97,8 @@ def test_attn_validation():
     far = 1 << 20
     assert call(st=[0, 0, 128, 0, 0, far, 0, 0, 128, 0, 0, 128]) == _lib.EUNSUPPORTED
     assert call(st=[0, 0, 128, 0, 0, 128, 0, 0, far, 0, 0, 128]) == _lib.EUNSUPPORTED
-    assert call(B=0) == _lib.EINVAL
+    assert call(B=-1) == _lib.EINVAL
+    assert call(H=-1) == _lib.EINVAL
     assert call(scale=0.0) == _lib.EINVAL
     assert call(scale=float("nan")) == _lib.EINVAL
     assert call(qp=None) == _lib.EINVAL
@@ -114,7 +115,7 @@ def test_dense_validation():
         return lib.varsparse_dense_attn_fwd(kw.get("dt", _lib.BF16), 1, 1, kw.get("d", 128), kw.get("nq", 10),
                                             kw.get("nk", 10), FAKE, FAKE, FAKE, FAKE, None,
                                             _strides(GOOD12), kw.get("scale", 0.1), None)
-    assert call(nq=0) == _lib.EINVAL
+    assert call(nq=-1) == _lib.EINVAL
     assert call(nk=0) == _lib.EINVAL
     assert call(d=32) == _lib.EUNSUPPORTED
     assert call(scale=-1.0) == _lib.EINVAL
@@ -146,7 +147,7 @@ def test_ocache_validation():
     p = ctypes.c_void_p(1 << 20)          # 16-byte aligned, never dereferenced: validation fails first
     call = lambda B=1, H=1, d=128, sd=32, stt=64, f=p, sp=p, o=p, strides=st: lib.varsparse_ocache_correct(
         B, H, d, sd, stt, f, sp, o, strides, None)
-    assert call(B=0) == _lib.EINVAL
+    assert call(B=-1) == _lib.EINVAL
     assert call(H=-1) == _lib.EINVAL
     assert call(d=12) == _lib.EINVAL                 # not a multiple of 8
     assert call(sd=0) == _lib.EINVAL
@@ -164,7 +165,7 @@ def test_join_validation():
     def call(sets=2, rows=64, nkb=172, join=0, ac=p, ai=q, bc=p, bi=q, oc=o1, oi=o2):
         return lib.varsparse_join_lists(sets, rows, nkb, join, ac, ai, 1, bc, bi, 0, oc, oi, None)
 
-    assert call(sets=0) == _lib.EINVAL
+    assert call(sets=-1) == _lib.EINVAL
     assert call(rows=0) == _lib.EINVAL
     assert call(nkb=0) == _lib.EINVAL
     assert call(nkb=65537) == _lib.EINVAL
@@ -220,7 +221,7 @@ def test_attn_pair_validation():
             kw.get("cnt", FAKE), FAKE, kw.get("per_head", 0), None)
     assert call(d=96) == _lib.EUNSUPPORTED
     assert call(g=_g(SCHEDULE_13, 4)) == _lib.EUNSUPPORTED    # 8x8 tiles only
-    assert call(B=0) == _lib.EINVAL
+    assert call(B=-1) == _lib.EINVAL
     assert call(scale=0.0) == _lib.EINVAL
     assert call(qp=None) == _lib.EINVAL
     assert call(cnt=None) == _lib.EINVAL
@@ -251,3 +252,42 @@ def test_map_indices_multi_validation():
     assert call(cnts=nulls) == _lib.EINVAL
     assert call(scores=None) == _lib.EINVAL
     assert call(sink=10) == _lib.EINVAL
+
+
+def test_empty_batch_is_a_no_op():
+    """B == 0 or H == 0 (dense: also nq == 0; join: sets == 0) returns OK with
+    every data pointer NULL once the geometry and scalars pass, so nothing is
+    read or enqueued; the same calls with a bad scalar still fail."""
+    lib = _lib.lib()
+    rad = (I32 * 32)(*([2] * 32))
+    st12 = _strides(GOOD12)
+    for B, H in ((0, 16), (2, 0), (0, 0)):
+        assert lib.varsparse_attn_fwd(_g(), 12, _lib.BF16, B, H, 128, None, None, None, None, None, None, 0.088,
+                                      None, None, 0, None) == _lib.OK
+        assert lib.varsparse_attn_fwd(_g(), 12, _lib.BF16, B, H, 128, None, None, None, None, None, None, 0.0,
+                                      None, None, 0, None) == _lib.EINVAL
+        assert lib.varsparse_attn_fwd(_g(), 12, _lib.BF16, B, H, 96, None, None, None, None, None, None, 0.088,
+                                      None, None, 0, None) == _lib.EUNSUPPORTED
+        assert lib.varsparse_attn_fwd_pair(_g(), 12, B, H, 128, None, None, None, None, None, None, 0.088, None,
+                                           None, 0, None) == _lib.OK
+        assert lib.varsparse_attn_fwd_token(_g(), 12, 5, rad, B, H, 128, None, None, None, None, None, None,
+                                            0.088, None, None, 0, None) == _lib.OK
+        assert lib.varsparse_attn_fwd_token(_g(), 12, 13, rad, B, H, 128, None, None, None, None, None, st12,
+                                            0.088, None, None, 0, None) == _lib.EINVAL
+        assert lib.varsparse_dense_attn_fwd(_lib.BF16, B, H, 128, 10, 10, None, None, None, None, None, None,
+                                            0.088, None) == _lib.OK
+        assert lib.varsparse_ocache_correct(B, H, 128, 32, 64, None, None, None, None, None) == _lib.OK
+        assert lib.varsparse_map_indices(_g(), 9, 12, 5, 0.9, _lib.BF16, B, H, 128, None, None, None, None, 0.088,
+                                         None, None, None, None, None, None) == _lib.OK
+        assert lib.varsparse_map_indices(_g(), 9, 12, 5, 0.0, _lib.BF16, B, H, 128, None, None, None, None, 0.088,
+                                         None, None, None, None, None, None) == _lib.EINVAL
+        assert lib.varsparse_map_indices_topk(_g(), 9, 12, 5, 0.2, _lib.BF16, B, H, 128, None, None, None, None,
+                                              0.088, None, None, None, None, None, None) == _lib.OK
+        ts = (I32 * 2)(10, 12)
+        nulls = (ctypes.c_void_p * 2)(None, None)
+        assert lib.varsparse_map_indices_multi(_g(), 9, 2, ts, 5, 0, 0.9, _lib.BF16, B, H, 128, None, None, None,
+                                               None, 0.088, None, nulls, nulls, None) == _lib.OK
+    assert lib.varsparse_dense_attn_fwd(_lib.BF16, 1, 1, 128, 0, 10, None, None, None, None, None, None,
+                                        0.088, None) == _lib.OK
+    assert lib.varsparse_join_lists(0, 64, 172, 0, None, None, 1, None, None, 0, None, None, None) == _lib.OK
+    assert lib.varsparse_join_lists(0, 64, 172, 2, None, None, 1, None, None, 0, None, None, None) == _lib.EINVAL
