@@ -209,6 +209,48 @@ def test_full_size_2b_last_scale_sampled_and_deterministic():
     _compare(od, ld, rdo, rdl, BF16_TOL, "2B dense full size")
 
 
+
+def test_key_value_offsets_at_the_addressing_limit():
+    """K and V rows as far apart as the bf16 kernels address: a token stride
+    that puts the last cached row's last byte just below 2^31 bytes from its
+    head's base (the per-head offsets are 32-bit), and a head stride that puts
+    the second head's base past 2^31 bytes (64-bit base).  The last query
+    tiles attend the last cached rows.  One more stride step is refused."""
+    vs = _vs()
+    w = W.LAST_SCALE_2B
+    B, H, d = 1, 2, w.d
+    q, k, v = spatial(w, B=B, H=H)
+    nk = k.shape[2]
+    st = ((2**31 - 1 - 2 * d) // (2 * (nk - 1))) // 8 * 8
+    assert (nk - 1) * st * 2 + 2 * d < 2**31 <= (nk - 1) * (st + 8) * 2 + 2 * d
+    assert nk * st * 2 > 2**31
+
+    def far(x):
+        buf = torch.empty(B * H * nk * st, dtype=torch.bfloat16, device="cuda")
+        view = buf.as_strided((B, H, nk, d), (H * nk * st, nk * st, st, 1))
+        view.copy_(to_device(x))
+        return view
+
+    qd, kd, vd = to_device(q), far(k), far(v)
+    cnt, idx, _ = vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, radius=w.radii)
+    o, lse = vs.attn_fwd(qd, kd, vd, w.sides, w.tile, w.q_scale, cnt, idx)
+    od, ld = vs.dense_attn_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    mc, mi = lists(oracle_mask(tuple(w.sides), w.q_scale, w.tile, w.n_sink, tuple(w.radii)))
+    bh = [(0, 0), (0, 1)]
+    ro, rl = OA.block_sparse_attention(q, k, v, w.sides, w.q_scale, w.tile, mc, mi, 1 / math.sqrt(d),
+                                       q_tiles=[0, 7, 56, 62, 63], bh=bh)
+    _compare(o, lse, ro, rl, BF16_TOL, "K/V offsets at the limit")
+    rows = [0, 4031, 4095]
+    rdo, rdl = OA.dense_attention(q, k, v, 1 / math.sqrt(d), q_rows=rows, bh=bh)
+    _compare(od, ld, rdo, rdl, BF16_TOL, "dense, K/V offsets at the limit")
+    wider = torch.empty(nk * (st + 8), dtype=torch.bfloat16, device="cuda").as_strided(
+        (1, 1, nk, d), (nk * (st + 8), nk * (st + 8), st + 8, 1))
+    with pytest.raises(vs.VarsparseError):
+        vs.attn_fwd(qd[:, :1], wider, wider, w.sides, w.tile, w.q_scale, cnt, idx)
+    del kd, vd, wider
+    torch.cuda.empty_cache()
+
 def test_full_size_high_res_sampled():
     """High-resolution stress: B=1, H=16, side 128 queries over 42521 tokens."""
     vs = _vs()
