@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0
 # over GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), recorded with the SHA-256 of the
 # kernel sources they were taken on; reported only while those sources are
 # unchanged.
-TRAFFIC = {"bytes": 431.7e6, "mfma_busy": 0.359, "sources_sha256": "ba006d216437868ef69510371fdb8f5dca05159b11b92f840590b4dd36a0ee5a"}
+TRAFFIC = {"bytes": 438.1e6, "mfma_busy": 0.346, "sources_sha256": "7f4e7a93f571a9866257e85575702dec795b5e8e90d2a0d5e6959c8d2ddcfdd3"}
 KERNEL_SOURCES = ("block_sparse_cross_csla_amd/csrc/attn_bf16.hip", "block_sparse_cross_csla_amd/csrc/common.h",
                   "block_sparse_cross_csla_amd/csrc/kernel_args.h")
 
@@ -562,8 +562,9 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
     schedule: dense below the decision scale (side 32); at it, full attention,
     scores + selection and block-sparse attention over its own selection; at
     sides 40/48/64, CS4A mapping joined (union) with the CSLA window lists of
-    windows 3/5/7, block-sparse attention and the O_cache correction.
-    Compared with dense attention at every scale."""
+    windows 3/5/7, then block-sparse attention with the O_cache correction in
+    its epilogue (one launch; the two-launch form, attention then correction,
+    is timed beside it).  Compared with dense attention at every scale."""
     w = W.CS4A
     D = W.CS4A_DECISION
     windows = (3, 5, 7)
@@ -593,7 +594,7 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
 
     multi_out = [lists_d] + [bufs[T][0] for T in W.CS4A_TARGETS]
 
-    def loop_step():
+    def loop_step(fused=True):
         for s in range(D + 1):
             dense_at(s)
         # the decision scale's scores and the lists of itself and every later scale, in one launch
@@ -605,9 +606,14 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
             mapped, window, joined, radius = bufs[T]
             vs.build_mask(w.sides, w.tile, T, w.n_sink, radius=radius, out=(*window, None), stream=stream)
             vs.join_lists(*mapped, *window, join="union", out=joined, stream=stream)
-            vs.attn_fwd(qs[T], k[:, :, : nks[T]], v[:, :, : nks[T]], w.sides, w.tile, T, *joined,
-                        softmax_scale=scale, out=outs[T], want_lse=False, stream=stream)
-            vs.ocache_correct(outs[D], o_sparse_d, outs[T], w.sides[D], w.sides[T], stream=stream)
+            if fused:
+                vs.attn_fwd_ocache(qs[T], k[:, :, : nks[T]], v[:, :, : nks[T]], w.sides, w.tile, T, *joined, D,
+                                   outs[D], o_sparse_d, softmax_scale=scale, out=outs[T], want_lse=False,
+                                   stream=stream)
+            else:
+                vs.attn_fwd(qs[T], k[:, :, : nks[T]], v[:, :, : nks[T]], w.sides, w.tile, T, *joined,
+                            softmax_scale=scale, out=outs[T], want_lse=False, stream=stream)
+                vs.ocache_correct(outs[D], o_sparse_d, outs[T], w.sides[D], w.sides[T], stream=stream)
 
     def dense_step():
         for s in range(n):
@@ -617,19 +623,25 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
         for s in range(D):
             dense_at(s)
 
+    # the four forms timed in turn, three rounds, median per form (slow clock
+    # drift then affects every form alike)
     reps = max(5, args.steps // 2)
-    res = {}
-    for name, fn in (("loop", loop_step), ("dense", dense_step), ("below_d", below_d)):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        res[name] = e0.elapsed_time(e1) / reps
+    forms = (("loop", loop_step), ("loop_two_launch", lambda: loop_step(fused=False)),
+             ("dense", dense_step), ("below_d", below_d))
+    runs = {name: [] for name, _ in forms}
+    for _ in range(3):
+        for name, fn in forms:
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            runs[name].append(e0.elapsed_time(e1) / reps)
+    res = {name: float(np.median(v)) for name, v in runs.items()}
     loop_step()
     torch.cuda.synchronize()
     sparsity = {}
@@ -644,11 +656,12 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
             "windows": list(windows), "join": "union", "top_p": W.CS4A_TOP_P,
             "ms_per_step": res["loop"], "dense_ms_per_step": res["dense"],
             "speedup_vs_dense": res["dense"] / res["loop"],
+            "ms_per_step_two_launch_ocache": res["loop_two_launch"],
             "dense_below_decision_ms": res["below_d"],
             "count_sparsity": sparsity,
             "timed": "dense attention at sides 1..24; at 32 dense + scores + one select/map launch for 32/40/48/64 + "
-                     "block-sparse over its own selection; at 40/48/64 CSLA window mask + union + block-sparse + "
-                     "O_cache; dense: all 13 scales"}
+                     "block-sparse over its own selection; at 40/48/64 CSLA window mask + union + block-sparse "
+                     "attention with the O_cache correction in its epilogue; dense: all 13 scales"}
 
 
 def cpu_baseline(w, q_np, k_np, v_np, cnt_h, idx_h, sizes, round_bf16, seconds):

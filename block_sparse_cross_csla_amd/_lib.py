@@ -27,6 +27,7 @@ EXPORTS = (
     "varsparse_attn_fwd",
     "varsparse_attn_fwd_token",
     "varsparse_attn_fwd_pair",
+    "varsparse_attn_fwd_ocache",
     "varsparse_dense_attn_fwd",
     "varsparse_ocache_correct",
     "varsparse_join_lists",
@@ -72,7 +73,9 @@ def _load():
     lib.varsparse_strerror.argtypes = [ctypes.c_int]
     lib.varsparse_strerror.restype = ctypes.c_char_p
     lib.varsparse_last_hip_error.argtypes = []
-    for name in EXPORTS[:12]:
+    lib.varsparse_attn_fwd_ocache.argtypes = [PG, I32, I32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32,
+                                              P, P, PI64, P]
+    for name in EXPORTS[:13]:
         getattr(lib, name).restype = ctypes.c_int
     lib.varsparse_last_hip_error.restype = ctypes.c_int
     return lib
@@ -367,6 +370,38 @@ def attn_fwd_pair(q, k, v, sides, tile: int, q_scale: int, kv_cnt, kv_idx, softm
     _check(_LIB.varsparse_attn_fwd_pair(ctypes.byref(g), q_scale, B, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                         _ptr(lse), _strides(q, k, v, out), float(scale), _ptr(kv_cnt), _ptr(kv_idx),
                                         per_head, _stream(stream)), "varsparse_attn_fwd_pair")
+    return out, lse
+
+
+def attn_fwd_ocache(q, k, v, sides, tile: int, q_scale: int, kv_cnt, kv_idx, d_scale: int, o_full_d, o_sparse_d,
+                    softmax_scale=None, out=None, lse=None, want_lse=True, stream=None):
+    """Block-sparse attention of a later scale with the O_cache correction
+    added before the output's rounding: attn_fwd followed by ocache_correct
+    in one pass (bf16).  o_full_d / o_sparse_d: the decision scale's full and
+    block-sparse outputs [B,H,side_d^2,d].  Returns (o, lse)."""
+    B, H, nq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, nq, dtype=torch.float32, device=q.device)
+    nqb, nkb, nq_s, nk_s = geom_counts(sides, tile, q_scale)
+    _check_qkvo(q, k, v, out, lse, nq_s, nk_s, bf16_only=True)
+    _check_lists(kv_cnt, kv_idx, B, H, nqb, nkb)
+    _need(0 <= d_scale <= q_scale, "the decision scale is at or below the query scale")
+    nd = geom_counts(sides, tile, d_scale)[2]
+    for name, t in (("o_full_d", o_full_d), ("o_sparse_d", o_sparse_d)):
+        _need(tuple(t.shape) == (B, H, nd, d) and t.dtype == torch.bfloat16,
+              f"{name} is a bfloat16 [{B}, {H}, {nd}, {d}] tensor")
+        _need(t.stride(-1) == 1, "the head dimension must be contiguous")
+    _on_gpu(q, k, v, out, lse, kv_cnt, kv_idx, o_full_d, o_sparse_d)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    per_head = 1 if kv_cnt.dim() == 3 else 0
+    g = make_geom(sides, tile)
+    ds = (ctypes.c_int64 * 6)(*o_full_d.stride()[:3], *o_sparse_d.stride()[:3])
+    _check(_LIB.varsparse_attn_fwd_ocache(ctypes.byref(g), q_scale, d_scale, B, H, d, _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(out), _ptr(lse), _strides(q, k, v, out), float(scale), _ptr(kv_cnt),
+                                          _ptr(kv_idx), per_head, _ptr(o_full_d), _ptr(o_sparse_d), ds,
+                                          _stream(stream)), "varsparse_attn_fwd_ocache")
     return out, lse
 
 

@@ -282,6 +282,47 @@ int varsparse_attn_fwd(const varsparse_geom* geom, int32_t q_scale, varsparse_dt
     return hip_status(vs::launch_attn_fp32(a, head_dim, false, (hipStream_t)stream));
 }
 
+int varsparse_attn_fwd_ocache(const varsparse_geom* geom, int32_t q_scale, int32_t d_scale, int32_t B, int32_t H,
+                              int32_t head_dim, const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int64_t strides[12], float softmax_scale, const int32_t* kv_cnt,
+                              const int32_t* kv_idx, int32_t lists_per_head, const void* o_full_d,
+                              const void* o_sparse_d, const int64_t d_strides[6], void* stream) {
+    int rc = check_geom(geom);
+    if (rc) return rc;
+    if (q_scale < 0 || q_scale >= geom->n_scales) return VARSPARSE_EINVAL;
+    if (geom->side[q_scale] % geom->tile != 0) return VARSPARSE_EINVAL;
+    if (d_scale < 0 || d_scale > q_scale) return VARSPARSE_EINVAL;
+    if (B < 0 || H < 0) return VARSPARSE_EINVAL;
+    if (lists_per_head != 0 && lists_per_head != 1) return VARSPARSE_EINVAL;
+    if (!scale_ok(softmax_scale)) return VARSPARSE_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;
+    if (geom->tile != 8) return VARSPARSE_EUNSUPPORTED;
+    if (B == 0 || H == 0) return VARSPARSE_OK;   // empty batch: nothing to compute
+    if (!q || !k || !v || !o || !strides || !kv_cnt || !kv_idx) return VARSPARSE_EINVAL;
+    if (!o_full_d || !o_sparse_d || !d_strides) return VARSPARSE_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VARSPARSE_EINVAL;
+    if (!aligned16(o_full_d) || !aligned16(o_sparse_d)) return VARSPARSE_EINVAL;
+    if (!strides_ok(strides, 12, 8) || !strides_ok(d_strides, 6, 8)) return VARSPARSE_EINVAL;
+    const vs::DevGeom g = vs::make_dev_geom(*geom, q_scale);
+    const int nqb = g.nb[q_scale] * g.nb[q_scale];
+    if ((int64_t)nqb * B * H > 0x7fffffff) return VARSPARSE_EINVAL;
+    if (!offsets_fit(g.tok_off[q_scale + 1], strides[5], strides[8], head_dim)) return VARSPARSE_EUNSUPPORTED;
+    vs::AttnArgs a{};
+    a.q = (const __bf16*)q; a.k = (const __bf16*)k; a.v = (const __bf16*)v; a.o = (__bf16*)o; a.lse = lse;
+    a.sq_b = strides[0]; a.sq_h = strides[1]; a.sq_t = strides[2];
+    a.sk_b = strides[3]; a.sk_h = strides[4]; a.sk_t = strides[5];
+    a.sv_b = strides[6]; a.sv_h = strides[7]; a.sv_t = strides[8];
+    a.so_b = strides[9]; a.so_h = strides[10]; a.so_t = strides[11];
+    a.B = B; a.H = H; a.scale_log2 = (float)(softmax_scale * kLog2e);
+    a.kv_cnt = kv_cnt; a.kv_idx = kv_idx; a.per_head = lists_per_head;
+    a.nqb = nqb; a.nkb = g.tile_base[q_scale + 1]; a.q_side = geom->side[q_scale]; a.g = g;
+    a.oc_full = (const __bf16*)o_full_d; a.oc_sparse = (const __bf16*)o_sparse_d;
+    a.sf_b = d_strides[0]; a.sf_h = d_strides[1]; a.sf_t = d_strides[2];
+    a.sp_b = d_strides[3]; a.sp_h = d_strides[4]; a.sp_t = d_strides[5];
+    a.oc_side = geom->side[d_scale];
+    return hip_status(vs::launch_attn_bf16(a, head_dim, false, (hipStream_t)stream));
+}
+
 int varsparse_attn_fwd_pair(const varsparse_geom* geom, int32_t q_scale, int32_t B, int32_t H, int32_t head_dim,
                             const void* q, const void* k, const void* v, void* o, float* lse,
                             const int64_t strides[12], float softmax_scale, const int32_t* kv_cnt,

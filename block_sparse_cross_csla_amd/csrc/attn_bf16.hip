@@ -700,8 +700,11 @@ __device__ __forceinline__ bool work_tile(const AttnArgs& a, int work, int nqt, 
     return true;
 }
 
-template <int D, bool DENSE, bool TOKEN>
-__global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a) {
+// OC: the O_cache correction of a later scale (the decision scale's full
+// minus sparse output at the query's nearest-upsampled decision token) is
+// added to the normalised output before its one rounding to bf16.
+template <int D, bool DENSE, bool TOKEN, bool OC>
+__device__ __forceinline__ void attn_fwd_bf16_body(const AttnArgs& a) {
     constexpr int KSTEPS = D / 16;
     constexpr int MBLK = D / 32;
     constexpr int STAGE = 32 * D * 2;
@@ -950,14 +953,39 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if (qvalid) {
         __bf16* op = a.o + b * a.so_b + h * a.so_h + tok * a.so_t;
+        if constexpr (OC) {
+            // decision token (floor(y h_D / h_q), floor(x h_D / h_q)) of query
+            // (y, x); y and x recomputed from the token (below 2^30) rather than
+            // kept live across the walk
+            const uint32_t hq = (uint32_t)a.q_side, sd = (uint32_t)a.oc_side;
+            const uint32_t y = (uint32_t)tok / hq, x = (uint32_t)tok - y * hq;
+            const int64_t s = (int64_t)(y * sd / hq) * sd + x * sd / hq;
+            const __bf16* fp = a.oc_full + b * a.sf_b + h * a.sf_h + s * a.sf_t;
+            const __bf16* pp = a.oc_sparse + b * a.sp_b + h * a.sp_h + s * a.sp_t;
 #pragma unroll
-        for (int mb = 0; mb < MBLK; ++mb) {
+            for (int mb = 0; mb < MBLK; ++mb) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                bf16x4 val;
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int j = 32 * mb + 8 * kk + 4 * g;
+                    const bf16x4 f = *(const bf16x4*)(fp + j);
+                    const bf16x4 p = *(const bf16x4*)(pp + j);
+                    bf16x4 val;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = (__bf16)(st.oacc[mb][4 * kk + e] * inv);
-                *(bf16x4*)(op + 32 * mb + 8 * kk + 4 * g) = val;
+                    for (int e = 0; e < 4; ++e)
+                        val[e] = (__bf16)(st.oacc[mb][4 * kk + e] * inv + ((float)f[e] - (float)p[e]));
+                    *(bf16x4*)(op + j) = val;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < MBLK; ++mb) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    bf16x4 val;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) val[e] = (__bf16)(st.oacc[mb][4 * kk + e] * inv);
+                    *(bf16x4*)(op + 32 * mb + 8 * kk + 4 * g) = val;
+                }
             }
         }
         if (a.lse != nullptr && g == 0) {
@@ -966,6 +994,17 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
                 l_tot > 0.0f ? (st.m_run + __builtin_log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
         }
     }
+}
+
+template <int D, bool DENSE, bool TOKEN>
+__global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a) {
+    attn_fwd_bf16_body<D, DENSE, TOKEN, false>(a);
+}
+
+// Block-sparse attention of a later scale with its O_cache correction.
+template <int D>
+__global__ __launch_bounds__(128, 2) void attn_fwd_ocache_bf16_kernel(const AttnArgs a) {
+    attn_fwd_bf16_body<D, false, false, true>(a);
 }
 
 // ---- dense attention over few query blocks: each block's keys split over P wave pairs
@@ -1510,13 +1549,16 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStre
             return launch_dense_split(attn_dense_split_kernel<64, 2>, blocks, 2, 2 * 4 * stage, a, stream);
         }
     }
+    const bool oc = a.oc_full != nullptr && !dense && !token;
     if (head_dim == 128) {
         if (dense) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true, false>), grid, block, 0, stream, a);
         else if (token) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false, true>), grid, block, 0, stream, a);
+        else if (oc) hipLaunchKernelGGL(attn_fwd_ocache_bf16_kernel<128>, grid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false, false>), grid, block, 0, stream, a);
     } else {
         if (dense) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true, false>), grid, block, 0, stream, a);
         else if (token) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false, true>), grid, block, 0, stream, a);
+        else if (oc) hipLaunchKernelGGL(attn_fwd_ocache_bf16_kernel<64>, grid, block, 0, stream, a);
         else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();

@@ -26,6 +26,11 @@ struct AttnArgs {
     int32_t radius[kMaxScales];
     // dense walk
     int64_t nq, nk;
+    // O_cache correction in the epilogue: decision-scale full and sparse outputs
+    const __bf16* oc_full;
+    const __bf16* oc_sparse;
+    int64_t sf_b, sf_h, sf_t, sp_b, sp_h, sp_t;
+    int32_t oc_side;
 };
 
 struct AttnF32Args {

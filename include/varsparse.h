@@ -309,6 +309,29 @@ int varsparse_ocache_correct(int32_t B, int32_t H, int32_t head_dim, int32_t sid
                              const void* o_full_d, const void* o_sparse_d, void* o_t,
                              const int64_t strides[9], void* stream);
 
+/*
+ * Block-sparse attention of a later scale with its O_cache correction, in one
+ * pass (SparVAR, ai.info summary, "Methodology in Plain English", first
+ * module: the later sparse outputs are corrected with the decision scale's
+ * cached residual).  For every query (y, x) of query scale q_scale and head
+ * dim c:
+ *     o[y, x, c] = A[y, x, c] + o_full_d[y', x', c] - o_sparse_d[y', x', c],
+ *     y' = floor(y side_d / side_q), x' = floor(x side_d / side_q),
+ * with A the attention varsparse_attn_fwd computes (same arguments, lists
+ * and lse) and side_d the side of decision scale d_scale <= q_scale: the
+ * result of varsparse_attn_fwd followed by varsparse_ocache_correct, with the
+ * sum taken in fp32 and rounded to bf16 once (not after the attention too).
+ * bf16 only, head_dim in {64, 128}, tile == 8.  o_full_d / o_sparse_d: dev
+ * bf16 [B, H, side_d^2, head_dim], 16-byte aligned, not overlapping o;
+ * d_strides: 6 element strides {full_b, full_h, full_t, sparse_b, sparse_h,
+ * sparse_t}, multiples of 8.
+ */
+int varsparse_attn_fwd_ocache(const varsparse_geom* geom, int32_t q_scale, int32_t d_scale, int32_t B, int32_t H,
+                              int32_t head_dim, const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int64_t strides[12], float softmax_scale, const int32_t* kv_cnt,
+                              const int32_t* kv_idx, int32_t lists_per_head, const void* o_full_d,
+                              const void* o_sparse_d, const int64_t d_strides[6], void* stream);
+
 /* Static description of a status code. */
 /* How varsparse_join_lists combines two kept-tile sets. */
 enum {

@@ -291,3 +291,26 @@ def test_empty_batch_is_a_no_op():
                                         0.088, None) == _lib.OK
     assert lib.varsparse_join_lists(0, 64, 172, 0, None, None, 1, None, None, 0, None, None, None) == _lib.OK
     assert lib.varsparse_join_lists(0, 64, 172, 2, None, None, 1, None, None, 0, None, None, None) == _lib.EINVAL
+
+
+def test_attn_ocache_validation():
+    lib = _lib.lib()
+    d6 = _strides([0, 0, 128] * 2)
+
+    def call(**kw):
+        return lib.varsparse_attn_fwd_ocache(
+            kw.get("g", _g()), kw.get("q", 12), kw.get("D", 9), kw.get("B", 2), kw.get("H", 16), kw.get("d", 128),
+            FAKE, FAKE, FAKE, FAKE, None, _strides(GOOD12), kw.get("scale", 0.088), FAKE, FAKE,
+            kw.get("per_head", 1), kw.get("f", FAKE), kw.get("p", FAKE), _strides(kw.get("ds", [0, 0, 128] * 2)),
+            None)
+    assert call(D=13) == _lib.EINVAL                          # decision scale above the query scale
+    assert call(D=-1) == _lib.EINVAL
+    assert call(f=None) == _lib.EINVAL
+    assert call(p=MISALIGNED) == _lib.EINVAL
+    assert call(ds=[0, 0, 130, 0, 0, 128]) == _lib.EINVAL    # decision rows not 16-byte aligned
+    assert call(d=96) == _lib.EUNSUPPORTED
+    assert call(g=_g(SCHEDULE_13, 4)) == _lib.EUNSUPPORTED    # 8x8 tiles only
+    assert call(B=-1) == _lib.EINVAL
+    assert call(per_head=2) == _lib.EINVAL
+    assert lib.varsparse_attn_fwd_ocache(_g(), 12, 9, 0, 16, 128, None, None, None, None, None, None, 0.088, None,
+                                         None, 0, None, None, d6, None) == _lib.OK     # empty batch

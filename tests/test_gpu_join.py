@@ -139,7 +139,8 @@ def test_scale_loop_stage_by_stage():
     """Each target scale's corrected output, given the GPU's own upstream
     results: the oracle's block-sparse attention over the GPU's joined lists,
     plus the nearest-upsampled residual of the GPU's decision-scale full and
-    sparse outputs (the oracle's O_cache correction), within 2e-2."""
+    sparse outputs (the oracle's O_cache correction), within 2e-2; both as two
+    launches (attention, then the correction) and as one."""
     from oracle import attention as OA, ocache as OO
     vs = _vs()
     w = W.CS4A
@@ -169,12 +170,17 @@ def test_scale_loop_stage_by_stage():
         o, _ = vs.attn_fwd(qd[T], kd[:, :, :nkT], vd[:, :, :nkT], w.sides, w.tile, T, jc, ji,
                            softmax_scale=scale, want_lse=False)
         vs.ocache_correct(o_full, o_sparse, o, w.sides[D], w.sides[T])
+        # the same step in one launch: the correction in the attention's epilogue
+        o1, _ = vs.attn_fwd_ocache(qd[T], kd[:, :, :nkT], vd[:, :, :nkT], w.sides, w.tile, T, jc, ji, D, o_full,
+                                   o_sparse, softmax_scale=scale, want_lse=False)
         torch.cuda.synchronize()
         ro, _ = OA.block_sparse_attention(qs[T], k[:, :, :nkT], v[:, :, :nkT], w.sides, T, w.tile,
                                           jc.cpu().numpy(), ji.cpu().numpy(), scale)
         want = OO.correct(ro, of, osp, w.sides[D], w.sides[T])
         err = np.abs(o.float().cpu().numpy() - want).max()
         assert err <= 2e-2, (T, err)
+        err1 = np.abs(o1.float().cpu().numpy() - want).max()
+        assert err1 <= 2e-2, (T, "one launch", err1)
 
 
 def test_scale_loop_matches_oracle():

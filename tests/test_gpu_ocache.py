@@ -7,14 +7,18 @@ unit in the last place of the result (relative 2^-8) plus an absolute 1e-6
 for results near zero.  Checked on random data at the decision/target sides
 of the CS4A workload (32 -> 40, 48, 64, and 32 -> 32), head dims 64 and 128,
 a non-contiguous target view, and end to end on the CS4A pipeline's own
-outputs (decision scale full and sparse attention, target sparse attention)."""
+outputs (decision scale full and sparse attention, target sparse attention).
+The fused form (attention with the correction added before its one rounding)
+is held to the oracle's exact attention plus the upsampled residual within
+the bf16 output bar, its lse bit for bit to the attention's, and to the
+two-call path within the second rounding the latter takes."""
 import math
 
 import numpy as np
 import pytest
 import torch
 
-from oracle import ocache as OO
+from oracle import attention as OA, ocache as OO
 from tests._common import spatial, to_device
 from varsparse_inputs import round_bf16, workloads as W
 
@@ -101,3 +105,48 @@ def test_cs4a_pipeline_outputs():
     vs.ocache_correct(o_full, o_sparse, o_t, w.sides[D], w.sides[T])
     torch.cuda.synchronize()
     _check(o_t, before, f, p, w.sides[D], w.sides[T], "cs4a pipeline")
+
+
+def _ulp_bf16(x):
+    """One bf16 unit in the last place of |x| (normal range)."""
+    return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126))) - 7)
+
+
+@pytest.mark.parametrize("ti,d", [(0, 128), (1, 128), (2, 128), (2, 64)])
+def test_fused_attention_with_correction(ti, d):
+    """varsparse_attn_fwd_ocache at the CS4A targets (sides 40, 48, 64) on the
+    pipeline's own decision outputs and target lists."""
+    vs = _vs()
+    w = W.CS4A
+    D, T = W.CS4A_DECISION, W.CS4A_TARGETS[ti]
+    B, H = 1, 2
+    q_t, k, v = spatial(w, B=B, H=H)
+    if d != w.d:
+        q_t, k, v = q_t[..., :d].copy(), k[..., :d].copy(), v[..., :d].copy()
+    q_d = spatial(w, B=B, H=H, q_side=w.sides[D])[0][..., :d].copy()
+    q_tt = spatial(w, B=B, H=H, q_side=w.sides[T])[0][..., :d].copy()
+    nk_d = sum(s * s for s in w.sides[: D + 1])
+    kd, vd, qd_dev, qt_dev = to_device(k), to_device(v), to_device(q_d), to_device(q_tt)
+    _, outs = vs.map_indices_multi(w.sides, w.tile, D, [D, T], w.n_sink, W.CS4A_TOP_P, q_d=qd_dev, k=kd)
+    (cnt_d, idx_d), (cnt_t, idx_t) = outs
+    o_full, _ = vs.dense_attn_fwd(qd_dev, kd[:, :, :nk_d], vd[:, :, :nk_d], want_lse=False)
+    o_sparse, _ = vs.attn_fwd(qd_dev, kd, vd, w.sides, w.tile, D, cnt_d, idx_d, want_lse=False)
+    o_two, lse_two = vs.attn_fwd(qt_dev, kd, vd, w.sides, w.tile, T, cnt_t, idx_t)
+    a_bf16 = o_two.clone()
+    vs.ocache_correct(o_full, o_sparse, o_two, w.sides[D], w.sides[T])
+    o_fused, lse_fused = vs.attn_fwd_ocache(qt_dev, kd, vd, w.sides, w.tile, T, cnt_t, idx_t, D, o_full, o_sparse)
+    torch.cuda.synchronize()
+    assert torch.equal(lse_fused, lse_two)
+    f, p = _bf16_np(o_full), _bf16_np(o_sparse)
+    assert np.abs(f - p).max() > 0, "the decision-scale selection dropped nothing: no residual to test"
+    a_exact, _ = OA.block_sparse_attention(q_tt, k, v, w.sides, T, w.tile, cnt_t.cpu().numpy(), idx_t.cpu().numpy(),
+                                           1 / math.sqrt(d))
+    ref = OO.correct(a_exact, f, p, w.sides[D], w.sides[T])
+    got, two, a = _bf16_np(o_fused), _bf16_np(o_two), _bf16_np(a_bf16)
+    err = np.abs(got - ref).max()
+    assert err <= 2e-2, f"fused vs oracle: {err}"
+    # the two-call path rounds the attention to bf16 before the correction:
+    # the results differ by at most that rounding plus each one's own
+    bound = 0.5 * _ulp_bf16(a) + _ulp_bf16(np.maximum(np.abs(got), np.abs(two))) + ABS_FLOOR
+    gap = np.abs(got - two)
+    assert (gap <= bound).all(), f"fused vs two calls: {int((gap > bound).sum())} values, max {gap.max()}"
