@@ -8,7 +8,8 @@ scale dropped), or a budget; two more cases keep no sink and drop every
 scale (every row empty) or all but the query scale's own window.  Checked on every query tile of every head:
 the CSLA lists bit for bit against the oracle's mask; block-sparse attention
 (64-query and paired-tile kernels), token-exact attention over the same
-lists and dense attention against the oracle, outputs and lse within 2e-2."""
+lists and dense attention against the oracle, outputs and lse within 2e-2;
+and the fp32 kernel on random schedules with other tile sides (1e-4)."""
 import math
 
 import numpy as np
@@ -95,3 +96,44 @@ def test_random_geometry(seed):
         torch.cuda.synchronize()
         rto, rtl = OA.token_masked_attention(q64, k64, v64, sides, qs, 8, n_sink, list(radius), scale)
         _cmp(ot, lset, rto, rtl, where + " (token-exact)")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_geometry_fp32(seed):
+    """The fp32 kernel (tiles of up to 64 tokens) on random schedules with
+    tile sides 3, 4, 5 and 8: lists bit-exact, block-sparse and dense
+    attention within 1e-4 of the oracle."""
+    vs = _vs()
+    rng = np.random.default_rng(9000 + seed)
+    t = int(rng.choice([3, 4, 5, 8]))
+    n = int(rng.integers(3, 7))
+    last = t * int(rng.integers(max(1, -(-n // t)), 24 // t + 1))
+    sides = tuple(int(x) for x in np.sort(rng.choice(np.arange(1, last), size=n - 1, replace=False))) + (last,)
+    qs = n - 1
+    n_sink = int(rng.integers(0, qs + 1))
+    radius = tuple(int(r) for r in rng.integers(-1, 3, size=n))
+    B, H, d = 1, int(rng.integers(1, 3)), int(rng.choice([64, 128]))
+    where = f"seed {seed}: sides {sides} tile {t} sink {n_sink} radius {radius} H {H} d {d}"
+    print(where, flush=True)
+    nqb, nkb, nq, nk = G.counts(sides, qs, t)
+    q, k, v = gaussian(500 + seed, 19, B, H, nq, nk, d, bf16=False)
+    scale = 1 / math.sqrt(d)
+    qd, kd, vd = (to_device(x, torch.float32) for x in (q, k, v))
+    cnt, idx, _ = vs.build_mask(sides, t, qs, n_sink, radius=radius)
+    o, lse = vs.attn_fwd(qd, kd, vd, sides, t, qs, cnt, idx, softmax_scale=scale)
+    od, lsed = vs.dense_attn_fwd(qd, kd, vd, softmax_scale=scale)
+    torch.cuda.synchronize()
+    mc, mi = L.lists_from_mask(L.block_mask(sides, qs, t, n_sink, list(radius)))
+    assert np.array_equal(cnt.cpu().numpy(), mc), where
+    assert np.array_equal(idx.cpu().numpy(), mi), where
+    q64, k64, v64 = q.astype(np.float64), k.astype(np.float64), v.astype(np.float64)
+    ro, rl = OA.block_sparse_attention(q64, k64, v64, sides, qs, t, mc, mi, scale)
+    rdo, rdl = OA.dense_attention(q64, k64, v64, scale)
+    for (og, lg, rfo, rfl, what) in ((o, lse, ro, rl, "block-sparse"), (od, lsed, rdo, rdl, "dense")):
+        err = np.abs(og.cpu().numpy() - rfo).max()
+        assert err <= 1e-4, f"{where} ({what}): max |O - O_ref| = {err}"
+        lgn = lg.cpu().numpy()
+        fin = np.isfinite(rfl)
+        assert np.isneginf(lgn[~fin]).all(), f"{where} ({what}): lse of empty rows"
+        if fin.any():
+            assert np.abs(lgn[fin] - rfl[fin]).max() <= 1e-4, f"{where} ({what}): lse"
