@@ -243,6 +243,17 @@ struct WaveState {
     // take as their immediate offset
     uint32_t koff[D / 16];
     uint32_t voff[D / 32][2];     // rows 16 t + ..: the swizzle repeats every 16 rows, so t adds 16 rows
+
+    // Called where the wave is about to wait for all its loads anyway: an
+    // empty asm that reads and rewrites the Q^T operands tells the compiler
+    // that their loads are complete.  Otherwise its own wait for them stays
+    // in front of the S^T MFMAs of every chunk step, and a vmcnt wait there
+    // also waits for the chunk loads issued after the barrier (asm, which the
+    // compiler does not count).
+    __device__ __forceinline__ void q_ready() {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) asm volatile("" : "+v"(qreg[s]));
+    }
 };
 
 // Fill the operand-read offsets of WaveState (once per kernel).  The values
@@ -898,6 +909,7 @@ __device__ __forceinline__ void attn_fwd_bf16_body(const AttnArgs& a) {
                 constexpr int S = decltype(stage_tag)::value ? 1 : 0;
                 // this wave's loads of chunk ci, and its V^T reads of chunk ci - 1 (whose
                 // stage the loads issued below overwrite), are complete on both waves
+                st.q_ready();
                 wait_all();
                 wg_barrier();
                 if (ci + 1 < nch) {
@@ -1082,6 +1094,7 @@ __global__ __launch_bounds__(128 * P, P == 2 ? 2 : 1) void attn_dense_split_kern
         if (nch > 0) load_chunk<D>(plan, kh, vh, krb, vrb, cur, L, L + STAGE, pw, lane);
         auto step = [&](auto stage_tag, auto ex_tag, int ci) {
             constexpr int S = decltype(stage_tag)::value ? 1 : 0;
+            st.q_ready();
             wait_all();
             wg_barrier();
             if (ci + 1 < nch) {
@@ -1451,6 +1464,11 @@ __global__ __launch_bounds__(256, 2) void attn_pair_bf16_kernel(const AttnArgs a
                                    wave, lane);
             }
         }
+        // Q^T complete from here on: the compiler's wait for it falls here, once
+        // per segment, and waits for the prefetched chunks too (issued back to
+        // back, so little beyond the first), not in front of the MFMAs of every
+        // chunk, where it would also wait for the loads running ahead
+        st.q_ready();
         for (int ci0 = 0; ci0 < nch; ci0 += NST) {
 #pragma unroll
             for (int u = 0; u < NST; ++u) {           // stage u holds chunk ci0 + u

@@ -164,6 +164,12 @@ __global__ __launch_bounds__(kScoreThreads) void cs4a_score_kernel(const ScoreAr
     for (int p = 0; p < kScoreParts; ++p) nmax = max(nmax, nchunks[p]);
     const ScoreChunk* mytab = table + par * tpp;
     wait_vmcnt(0);   // Q is in registers before LDS-DMA traffic starts
+    // ... and the compiler is told so (an empty asm that reads and rewrites
+    // the operands): otherwise its own waits for the Q loads stay in front of
+    // the MFMAs of every chunk, where a vmcnt wait also waits for the chunk
+    // loads running ahead (asm, which it does not count)
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(qreg[s]));
 
     const lds_ptr kst0 = (lds_ptr)kst_base + par * NST * STAGE;
     auto issue = [&](int ci) {
@@ -353,6 +359,12 @@ __global__ __launch_bounds__(kScore2Threads) void cs4a_score2_kernel(const Score
     for (int p = 0; p < kScoreParts; ++p) nmax = max(nmax, nchunks[p]);
     const ScoreChunk* mytab = table + par * tpp;
     wait_vmcnt(0);   // Q is in registers before LDS-DMA traffic starts
+    // ... and the compiler is told so (an empty asm that reads and rewrites
+    // the operands): otherwise its own waits for the Q loads stay in front of
+    // the MFMAs of every chunk, where a vmcnt wait also waits for the chunk
+    // loads running ahead (asm, which it does not count)
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(qreg[s]));
 
     const lds_ptr kst0 = (lds_ptr)kst_base + par * NST * STAGE;
     auto issue = [&](int ci) {
