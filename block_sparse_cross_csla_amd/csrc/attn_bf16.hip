@@ -1533,12 +1533,11 @@ hipError_t launch_attn_pair_bf16(const AttnArgs& a, int head_dim, hipStream_t st
 
 namespace {
 
-template <typename K>
-hipError_t launch_dense_split(K kernel, int64_t blocks, int parts, size_t shmem, const AttnArgs& a,
-                              hipStream_t stream) {
-    const hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+template <auto Kernel>
+hipError_t launch_dense_split(int64_t blocks, int parts, size_t shmem, const AttnArgs& a, hipStream_t stream) {
+    const hipError_t e = allow_dynamic_lds<Kernel>(shmem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(128 * parts), shmem, stream, a);
+    hipLaunchKernelGGL(Kernel, dim3((unsigned)blocks), dim3(128 * parts), shmem, stream, a);
     return hipGetLastError();
 }
 
@@ -1558,13 +1557,13 @@ hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStre
         const size_t stage = (size_t)32 * head_dim * 2;
         if (blocks <= 256 && nch_all >= 24) {
             if (head_dim == 128)
-                return launch_dense_split(attn_dense_split_kernel<128, 4>, blocks, 4, 4 * 4 * stage, a, stream);
-            return launch_dense_split(attn_dense_split_kernel<64, 4>, blocks, 4, 4 * 4 * stage, a, stream);
+                return launch_dense_split<attn_dense_split_kernel<128, 4>>(blocks, 4, 4 * 4 * stage, a, stream);
+            return launch_dense_split<attn_dense_split_kernel<64, 4>>(blocks, 4, 4 * 4 * stage, a, stream);
         }
         if (blocks <= 512 && nch_all >= 12) {
             if (head_dim == 128)
-                return launch_dense_split(attn_dense_split_kernel<128, 2>, blocks, 2, 2 * 4 * stage, a, stream);
-            return launch_dense_split(attn_dense_split_kernel<64, 2>, blocks, 2, 2 * 4 * stage, a, stream);
+                return launch_dense_split<attn_dense_split_kernel<128, 2>>(blocks, 2, 2 * 4 * stage, a, stream);
+            return launch_dense_split<attn_dense_split_kernel<64, 2>>(blocks, 2, 2 * 4 * stage, a, stream);
         }
     }
     const bool oc = a.oc_full != nullptr && !dense && !token;

@@ -4,9 +4,32 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "varsparse.h"
 
 namespace vs {
+
+// Host: let `Kernel` launch with up to `bytes` of dynamic LDS on the current
+// device.  The attribute belongs to the function on each device and only
+// grows, so the runtime is called once per (kernel, device, larger size):
+// repeated launches, and launches under stream capture, make no such call.
+// A mutex keeps the recorded size equal to the attribute when threads race.
+template <auto Kernel>
+hipError_t allow_dynamic_lds(size_t bytes) {
+    constexpr int kDevices = 64;
+    static std::mutex mu;
+    static size_t granted[kDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool tracked = dev >= 0 && dev < kDevices;
+    std::lock_guard<std::mutex> lock(mu);
+    if (tracked && granted[dev] >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute((const void*)Kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess && tracked) granted[dev] = bytes;
+    return e;
+}
 
 constexpr int kMaxScales = VARSPARSE_MAX_SCALES;
 

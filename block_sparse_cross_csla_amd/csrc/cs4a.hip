@@ -623,11 +623,11 @@ size_t score_shmem(int parts, int stages, int head_dim, int nkb, int nq) {
            (size_t)nkb * nq * sizeof(float);   // 12: padding to the 16-byte aligned float arrays
 }
 
-template <typename K>
-hipError_t launch_with_shmem(K kernel, dim3 grid, dim3 block, size_t shmem, const ScoreArgs& a, hipStream_t stream) {
-    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+template <auto Kernel>
+hipError_t launch_with_shmem(dim3 grid, dim3 block, size_t shmem, const ScoreArgs& a, hipStream_t stream) {
+    const hipError_t e = allow_dynamic_lds<Kernel>(shmem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, a);
+    hipLaunchKernelGGL(Kernel, grid, block, shmem, stream, a);
     return hipGetLastError();
 }
 
@@ -642,16 +642,16 @@ hipError_t launch_cs4a_score(const ScoreArgs& a, int head_dim, hipStream_t strea
     const size_t s4 = score_shmem(kScoreParts, 4, head_dim, a.nkb, 128);
     const size_t s3 = score_shmem(kScoreParts, 3, head_dim, a.nkb, 128);
     if (head_dim == 128) {
-        if (s4 <= kLdsBytes) return launch_with_shmem(cs4a_score2_kernel<128, 4>, grid2, block2, s4, a, stream);
-        if (s3 <= kLdsBytes) return launch_with_shmem(cs4a_score2_kernel<128, 3>, grid2, block2, s3, a, stream);
+        if (s4 <= kLdsBytes) return launch_with_shmem<cs4a_score2_kernel<128, 4>>(grid2, block2, s4, a, stream);
+        if (s3 <= kLdsBytes) return launch_with_shmem<cs4a_score2_kernel<128, 3>>(grid2, block2, s3, a, stream);
     } else {
-        if (s4 <= kLdsBytes) return launch_with_shmem(cs4a_score2_kernel<64, 4>, grid2, block2, s4, a, stream);
-        if (s3 <= kLdsBytes) return launch_with_shmem(cs4a_score2_kernel<64, 3>, grid2, block2, s3, a, stream);
+        if (s4 <= kLdsBytes) return launch_with_shmem<cs4a_score2_kernel<64, 4>>(grid2, block2, s4, a, stream);
+        if (s3 <= kLdsBytes) return launch_with_shmem<cs4a_score2_kernel<64, 3>>(grid2, block2, s3, a, stream);
     }
     const size_t shmem = score_shmem(kScoreParts, kScoreStages, head_dim, a.nkb, 64);
     const dim3 grid((unsigned)(a.nqb * a.B * a.H)), block(kScoreThreads);
-    if (head_dim == 128) return launch_with_shmem(cs4a_score_kernel<128>, grid, block, shmem, a, stream);
-    return launch_with_shmem(cs4a_score_kernel<64>, grid, block, shmem, a, stream);
+    if (head_dim == 128) return launch_with_shmem<cs4a_score_kernel<128>>(grid, block, shmem, a, stream);
+    return launch_with_shmem<cs4a_score_kernel<64>>(grid, block, shmem, a, stream);
 }
 
 hipError_t launch_cs4a_select_map(const SelMapArgs& a, int bh, hipStream_t stream) {
