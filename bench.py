@@ -345,11 +345,17 @@ def bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev):
     scale = 1.0 / math.sqrt(w.d)
 
     target_lists = [lists[T] for T in W.CS4A_TARGETS]
+    by_size = W.CS4A_TARGETS[::-1]   # largest target first: its longer walks start first
 
-    def step():
+    def step(one_launch=True):
         # scores at the decision scale, then the lists of the three targets in one launch
         vs.map_indices_multi(w.sides, w.tile, D, W.CS4A_TARGETS, w.n_sink, W.CS4A_TOP_P, q_d=q_d, k=k,
                              scores=scores, out=target_lists, stream=stream)
+        if one_launch:   # the three target attentions in one launch
+            vs.attn_fwd_multi([qs[T] for T in by_size], k, v, w.sides, w.tile, by_size,
+                              [lists[T] for T in by_size], softmax_scale=scale, outs=[outs[T] for T in by_size],
+                              want_lse=False, stream=stream)
+            return
         for T in W.CS4A_TARGETS:
             vs.attn_fwd(qs[T], k[:, :, : nks[T]], v[:, :, : nks[T]], w.sides, w.tile, T, *lists[T],
                         softmax_scale=scale, out=outs[T], want_lse=False, stream=stream)
@@ -361,7 +367,7 @@ def bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev):
 
     n = max(5, args.steps // 2)
     res = {}
-    for name, fn in (("sparse", step), ("dense", dense_step)):
+    for name, fn in (("sparse", step), ("sparse_three_launches", lambda: step(False)), ("dense", dense_step)):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -420,8 +426,9 @@ def bench_cs4a(vs, torch, W, SpatialField, to_dev, args, stream, dev):
             "speedup_vs_dense": res["dense"] / res["sparse"],
             "attention_tflop_per_step": flops / 1e12,
             "effective_tflops": flops / (res["sparse"] * 1e-3) / 1e12,
-            "timed": "score + one select/map launch for the 3 targets + 3 block-sparse attentions; "
-                     "dense: 3 dense attentions",
+            "ms_per_step_three_attention_launches": res["sparse_three_launches"],
+            "timed": "score + one select/map launch for the 3 targets + the 3 block-sparse attentions in one "
+                     "launch; dense: 3 dense attentions",
             "ocache": {"ms_per_step": res["ocache"],
                        "timed": "map D->D + block-sparse attention at D + 3 corrections",
                        "decision_full_attention_ms": res["full_d"],
@@ -606,6 +613,8 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
             mapped, window, joined, radius = bufs[T]
             vs.build_mask(w.sides, w.tile, T, w.n_sink, radius=radius, out=(*window, None), stream=stream)
             vs.join_lists(*mapped, *window, join="union", out=joined, stream=stream)
+            if fused == "multi":
+                continue
             if fused:
                 vs.attn_fwd_ocache(qs[T], k[:, :, : nks[T]], v[:, :, : nks[T]], w.sides, w.tile, T, *joined, D,
                                    outs[D], o_sparse_d, softmax_scale=scale, out=outs[T], want_lse=False,
@@ -614,6 +623,11 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
                 vs.attn_fwd(qs[T], k[:, :, : nks[T]], v[:, :, : nks[T]], w.sides, w.tile, T, *joined,
                             softmax_scale=scale, out=outs[T], want_lse=False, stream=stream)
                 vs.ocache_correct(outs[D], o_sparse_d, outs[T], w.sides[D], w.sides[T], stream=stream)
+        if fused == "multi":   # the three corrected target attentions in one launch, largest first
+            by_size = W.CS4A_TARGETS[::-1]
+            vs.attn_fwd_multi([qs[T] for T in by_size], k, v, w.sides, w.tile, by_size,
+                              [bufs[T][2] for T in by_size], softmax_scale=scale, outs=[outs[T] for T in by_size],
+                              want_lse=False, d_scale=D, o_full_d=outs[D], o_sparse_d=o_sparse_d, stream=stream)
 
     def dense_step():
         for s in range(n):
@@ -626,7 +640,8 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
     # the four forms timed in turn, three rounds, median per form (slow clock
     # drift then affects every form alike)
     reps = max(5, args.steps // 2)
-    forms = (("loop", loop_step), ("loop_two_launch", lambda: loop_step(fused=False)),
+    forms = (("loop", lambda: loop_step(fused="multi")), ("loop_per_target", loop_step),
+             ("loop_two_launch", lambda: loop_step(fused=False)),
              ("dense", dense_step), ("below_d", below_d))
     runs = {name: [] for name, _ in forms}
     for _ in range(3):
@@ -642,7 +657,7 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
             torch.cuda.synchronize()
             runs[name].append(e0.elapsed_time(e1) / reps)
     res = {name: float(np.median(v)) for name, v in runs.items()}
-    loop_step()
+    loop_step(fused="multi")
     torch.cuda.synchronize()
     sparsity = {}
     for T in W.CS4A_TARGETS:
@@ -656,12 +671,14 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
             "windows": list(windows), "join": "union", "top_p": W.CS4A_TOP_P,
             "ms_per_step": res["loop"], "dense_ms_per_step": res["dense"],
             "speedup_vs_dense": res["dense"] / res["loop"],
+            "ms_per_step_one_launch_per_target": res["loop_per_target"],
             "ms_per_step_two_launch_ocache": res["loop_two_launch"],
             "dense_below_decision_ms": res["below_d"],
             "count_sparsity": sparsity,
             "timed": "dense attention at sides 1..24; at 32 dense + scores + one select/map launch for 32/40/48/64 + "
-                     "block-sparse over its own selection; at 40/48/64 CSLA window mask + union + block-sparse "
-                     "attention with the O_cache correction in its epilogue; dense: all 13 scales"}
+                     "block-sparse over its own selection; at 40/48/64 CSLA window mask + union, then one "
+                     "block-sparse attention launch over the three with the O_cache correction in its epilogue; "
+                     "dense: all 13 scales"}
 
 
 def cpu_baseline(w, q_np, k_np, v_np, cnt_h, idx_h, sizes, round_bf16, seconds):

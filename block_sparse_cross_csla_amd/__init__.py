@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     OK,
     VarsparseError,
     attn_fwd,
+    attn_fwd_multi,
     attn_fwd_ocache,
     attn_fwd_pair,
     attn_fwd_token,

@@ -14,6 +14,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarsparse.so")
 MAX_SCALES = 32
+MAX_ATTN_TARGETS = 3
 BF16, FP32 = 0, 1
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 
@@ -28,6 +29,7 @@ EXPORTS = (
     "varsparse_attn_fwd_token",
     "varsparse_attn_fwd_pair",
     "varsparse_attn_fwd_ocache",
+    "varsparse_attn_fwd_multi",
     "varsparse_dense_attn_fwd",
     "varsparse_ocache_correct",
     "varsparse_join_lists",
@@ -75,7 +77,9 @@ def _load():
     lib.varsparse_last_hip_error.argtypes = []
     lib.varsparse_attn_fwd_ocache.argtypes = [PG, I32, I32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32,
                                               P, P, PI64, P]
-    for name in EXPORTS[:13]:
+    lib.varsparse_attn_fwd_multi.argtypes = [PG, I32, PI32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32,
+                                             I32, P, P, PI64, P]
+    for name in EXPORTS[:14]:
         getattr(lib, name).restype = ctypes.c_int
     lib.varsparse_last_hip_error.restype = ctypes.c_int
     return lib
@@ -403,6 +407,56 @@ def attn_fwd_ocache(q, k, v, sides, tile: int, q_scale: int, kv_cnt, kv_idx, d_s
                                           _ptr(kv_idx), per_head, _ptr(o_full_d), _ptr(o_sparse_d), ds,
                                           _stream(stream)), "varsparse_attn_fwd_ocache")
     return out, lse
+
+
+def attn_fwd_multi(qs, k, v, sides, tile: int, q_scales, lists, softmax_scale=None, outs=None, lses=None,
+                   want_lse=True, d_scale=None, o_full_d=None, o_sparse_d=None, stream=None):
+    """Block-sparse attention of several query scales over one cache in one
+    launch (bf16): target i is what attn_fwd (or, with the decision outputs
+    o_full_d / o_sparse_d of d_scale, attn_fwd_ocache) returns for q_scales[i],
+    qs[i] and lists[i] = (kv_cnt, kv_idx).  Returns [(o, lse) per target]."""
+    q_scales = [int(t) for t in q_scales]
+    n = len(q_scales)
+    _need(1 <= n <= MAX_ATTN_TARGETS, f"one to {MAX_ATTN_TARGETS} target scales")
+    _need(len(qs) == n and len(lists) == n, "one query tensor and one list pair per target")
+    B, H, _, d = qs[0].shape
+    if outs is None:
+        outs = [torch.empty_like(q) for q in qs]
+    if lses is None:
+        lses = [torch.empty(B, H, q.shape[2], dtype=torch.float32, device=q.device) if want_lse else None
+                for q in qs]
+    _need(len(outs) == n and len(lses) == n, "one output and one lse (or None) per target")
+    per_head = 1 if lists[0][0].dim() == 3 else 0
+    oc = o_full_d is not None or o_sparse_d is not None
+    strides = []
+    for t, q, out, lse, (c, i) in zip(q_scales, qs, outs, lses, lists):
+        nqb, nkb, nq_s, nk_s = geom_counts(sides, tile, t)
+        _need(q.shape[0] == B and q.shape[1] == H and q.shape[3] == d, "every target has q's B, H and head_dim")
+        _check_qkvo(q, k, v, out, lse, nq_s, nk_s, bf16_only=True)
+        _check_lists(c, i, B, H, nqb, nkb)
+        _need((1 if c.dim() == 3 else 0) == per_head, "lists all shared or all per (b, h)")
+        strides.extend(_strides(q, k, v, out))
+        if oc:
+            _need(d_scale is not None and 0 <= d_scale <= t, "the decision scale is at or below every target")
+    ds = None
+    if oc:
+        _need(o_full_d is not None and o_sparse_d is not None, "both decision-scale outputs, or neither")
+        nd = geom_counts(sides, tile, d_scale)[2]
+        for name, t in (("o_full_d", o_full_d), ("o_sparse_d", o_sparse_d)):
+            _need(tuple(t.shape) == (B, H, nd, d) and t.dtype == torch.bfloat16,
+                  f"{name} is a bfloat16 [{B}, {H}, {nd}, {d}] tensor")
+            _need(t.stride(-1) == 1, "the head dimension must be contiguous")
+        ds = (ctypes.c_int64 * 6)(*o_full_d.stride()[:3], *o_sparse_d.stride()[:3])
+    _on_gpu(*qs, k, v, *outs, *lses, *[x for pair in lists for x in pair], o_full_d, o_sparse_d)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    g = make_geom(sides, tile)
+    ptrs = lambda ts: (ctypes.c_void_p * n)(*[None if t is None else t.data_ptr() for t in ts])
+    _check(_LIB.varsparse_attn_fwd_multi(ctypes.byref(g), n, (ctypes.c_int32 * n)(*q_scales), B, H, d, ptrs(qs),
+                                         _ptr(k), _ptr(v), ptrs(outs), ptrs(lses), (ctypes.c_int64 * len(strides))(*strides),
+                                         float(scale), ptrs([c for c, _ in lists]), ptrs([i for _, i in lists]),
+                                         per_head, -1 if d_scale is None else int(d_scale), _ptr(o_full_d),
+                                         _ptr(o_sparse_d), ds, _stream(stream)), "varsparse_attn_fwd_multi")
+    return list(zip(outs, lses))
 
 
 def attn_fwd_token(q, k, v, sides, tile: int, q_scale: int, n_sink: int, radius, kv_cnt=None, kv_idx=None,

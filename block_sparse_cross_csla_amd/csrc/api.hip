@@ -323,6 +323,69 @@ int varsparse_attn_fwd_ocache(const varsparse_geom* geom, int32_t q_scale, int32
     return hip_status(vs::launch_attn_bf16(a, head_dim, false, (hipStream_t)stream));
 }
 
+int varsparse_attn_fwd_multi(const varsparse_geom* geom, int32_t n_targets, const int32_t* q_scales, int32_t B,
+                             int32_t H, int32_t head_dim, const void* const* q, const void* k, const void* v,
+                             void* const* o, float* const* lse, const int64_t* strides, float softmax_scale,
+                             const int32_t* const* kv_cnt, const int32_t* const* kv_idx, int32_t lists_per_head,
+                             int32_t d_scale, const void* o_full_d, const void* o_sparse_d,
+                             const int64_t d_strides[6], void* stream) {
+    int rc = check_geom(geom);
+    if (rc) return rc;
+    if (n_targets < 1 || n_targets > VARSPARSE_MAX_ATTN_TARGETS || !q_scales) return VARSPARSE_EINVAL;
+    const bool oc = o_full_d != nullptr || o_sparse_d != nullptr;
+    for (int i = 0; i < n_targets; ++i) {
+        const int t = q_scales[i];
+        if (t < 0 || t >= geom->n_scales || geom->side[t] % geom->tile != 0) return VARSPARSE_EINVAL;
+        if (oc && (d_scale < 0 || d_scale > t)) return VARSPARSE_EINVAL;
+    }
+    if (B < 0 || H < 0) return VARSPARSE_EINVAL;
+    if (lists_per_head != 0 && lists_per_head != 1) return VARSPARSE_EINVAL;
+    if (!scale_ok(softmax_scale)) return VARSPARSE_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;
+    if (geom->tile != 8) return VARSPARSE_EUNSUPPORTED;
+    if (B == 0 || H == 0) return VARSPARSE_OK;   // empty batch: nothing to compute
+    if (!q || !o || !k || !v || !strides || !kv_cnt || !kv_idx) return VARSPARSE_EINVAL;
+    if (!aligned16(k) || !aligned16(v)) return VARSPARSE_EINVAL;
+    if (oc) {
+        if (!o_full_d || !o_sparse_d || !d_strides) return VARSPARSE_EINVAL;
+        if (!aligned16(o_full_d) || !aligned16(o_sparse_d) || !strides_ok(d_strides, 6, 8)) return VARSPARSE_EINVAL;
+    }
+    int64_t blocks = 0;
+    vs::MultiAttnArgs m{};
+    m.n_targets = n_targets;
+    for (int i = 0; i < n_targets; ++i) {
+        const int t = q_scales[i];
+        const int64_t* st = strides + 12 * i;
+        if (!q[i] || !o[i] || !kv_cnt[i] || !kv_idx[i]) return VARSPARSE_EINVAL;
+        if (!aligned16(q[i]) || !aligned16(o[i])) return VARSPARSE_EINVAL;
+        if (!strides_ok(st, 12, 8)) return VARSPARSE_EINVAL;
+        for (int j = 3; j < 9; ++j)   // one cache: every target reads K and V alike
+            if (st[j] != strides[j]) return VARSPARSE_EINVAL;
+        const vs::DevGeom g = vs::make_dev_geom(*geom, t);
+        const int nqb = g.nb[t] * g.nb[t];
+        if (!offsets_fit(g.tok_off[t + 1], st[5], st[8], head_dim)) return VARSPARSE_EUNSUPPORTED;
+        blocks += (int64_t)nqb * B * H;
+        vs::AttnArgs& a = m.t[i];
+        a.q = (const __bf16*)q[i]; a.k = (const __bf16*)k; a.v = (const __bf16*)v; a.o = (__bf16*)o[i];
+        a.lse = lse != nullptr ? lse[i] : nullptr;
+        a.sq_b = st[0]; a.sq_h = st[1]; a.sq_t = st[2];
+        a.sk_b = st[3]; a.sk_h = st[4]; a.sk_t = st[5];
+        a.sv_b = st[6]; a.sv_h = st[7]; a.sv_t = st[8];
+        a.so_b = st[9]; a.so_h = st[10]; a.so_t = st[11];
+        a.B = B; a.H = H; a.scale_log2 = (float)(softmax_scale * kLog2e);
+        a.kv_cnt = kv_cnt[i]; a.kv_idx = kv_idx[i]; a.per_head = lists_per_head;
+        a.nqb = nqb; a.nkb = g.tile_base[t + 1]; a.q_side = geom->side[t]; a.g = g;
+        if (oc) {
+            a.oc_full = (const __bf16*)o_full_d; a.oc_sparse = (const __bf16*)o_sparse_d;
+            a.sf_b = d_strides[0]; a.sf_h = d_strides[1]; a.sf_t = d_strides[2];
+            a.sp_b = d_strides[3]; a.sp_h = d_strides[4]; a.sp_t = d_strides[5];
+            a.oc_side = geom->side[d_scale];
+        }
+    }
+    if (blocks > 0x7fffffff) return VARSPARSE_EINVAL;
+    return hip_status(vs::launch_attn_multi_bf16(m, head_dim, (hipStream_t)stream));
+}
+
 int varsparse_attn_fwd_pair(const varsparse_geom* geom, int32_t q_scale, int32_t B, int32_t H, int32_t head_dim,
                             const void* q, const void* k, const void* v, void* o, float* lse,
                             const int64_t strides[12], float softmax_scale, const int32_t* kv_cnt,

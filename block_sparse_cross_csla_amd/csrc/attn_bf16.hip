@@ -714,8 +714,10 @@ __device__ __forceinline__ bool work_tile(const AttnArgs& a, int work, int nqt, 
 // OC: the O_cache correction of a later scale (the decision scale's full
 // minus sparse output at the query's nearest-upsampled decision token) is
 // added to the normalised output before its one rounding to bf16.
-template <int D, bool DENSE, bool TOKEN, bool OC>
-__device__ __forceinline__ void attn_fwd_bf16_body(const AttnArgs& a) {
+// MULTI: the work item is given (a launch over several targets), else taken
+// from the workgroup id.
+template <int D, bool DENSE, bool TOKEN, bool OC, bool MULTI = false>
+__device__ __forceinline__ void attn_fwd_bf16_body(const AttnArgs& a, const int work_in = 0) {
     constexpr int KSTEPS = D / 16;
     constexpr int MBLK = D / 32;
     constexpr int STAGE = 32 * D * 2;
@@ -726,7 +728,7 @@ __device__ __forceinline__ void attn_fwd_bf16_body(const AttnArgs& a) {
     const int n = lane & 31, g = lane >> 5;  // query column and lane half of this lane
 
     const int64_t nqt = DENSE ? (a.nq + 63) / 64 : a.nqb;
-    const int work = xcd_remap(blockIdx.x, gridDim.x);
+    const int work = MULTI ? work_in : xcd_remap(blockIdx.x, gridDim.x);
     int bh, qt;
     LaneGeom lg;
     int ranked_count = 0;
@@ -1017,6 +1019,44 @@ __global__ __launch_bounds__(128, 2) void attn_fwd_bf16_kernel(const AttnArgs a)
 template <int D>
 __global__ __launch_bounds__(128, 2) void attn_fwd_ocache_bf16_kernel(const AttnArgs a) {
     attn_fwd_bf16_body<D, false, false, true>(a);
+}
+
+// Block-sparse attention of several query scales over one cache in one
+// launch (with or without the O_cache correction).  Each workgroup runs the
+// walk of attn_fwd_bf16_kernel for one work item of one target, so every
+// output is bit-identical to that target's own launch; one grid over all the
+// targets fills the chip where a small scale alone would leave CUs idle and
+// pay its own launch ramp and tail.  Work order: head pairs outermost (every
+// target of a head attends to the same cache, so one XCD's L2 holds the K/V
+// of its few heads for all of them), then the targets in the caller's order,
+// then the pair's items as attn_fwd_bf16_kernel orders one target's.
+template <int D, bool OC>
+__global__ __launch_bounds__(128, 2) void attn_multi_bf16_kernel(const MultiAttnArgs m) {
+    const int G = xcd_remap(blockIdx.x, gridDim.x);
+    const int n_bh = m.t[0].B * m.t[0].H, full_pairs = n_bh >> 1;
+    int sum2 = 0;
+#pragma unroll
+    for (int t = 0; t < kMaxAttnTargets; ++t)
+        if (t < m.n_targets) sum2 += 2 * m.t[t].nqb;
+    int p, r, mult;
+    if (G < full_pairs * sum2) {
+        p = G / sum2;
+        r = G - p * sum2;
+        mult = 2;
+    } else {   // the last head of an odd count: a pair of one
+        p = full_pairs;
+        r = G - full_pairs * sum2;
+        mult = 1;
+    }
+    int t = 0;
+#pragma unroll
+    for (int u = 0; u + 1 < kMaxAttnTargets; ++u) {
+        if (t == u && u + 1 < m.n_targets && r >= mult * m.t[u].nqb) {
+            r -= mult * m.t[u].nqb;
+            t = u + 1;
+        }
+    }
+    attn_fwd_bf16_body<D, false, false, OC, true>(m.t[t], 2 * p * m.t[t].nqb + r);
 }
 
 // ---- dense attention over few query blocks: each block's keys split over P wave pairs
@@ -1542,6 +1582,21 @@ hipError_t launch_dense_split(int64_t blocks, int parts, size_t shmem, const Att
 }
 
 }  // namespace
+
+hipError_t launch_attn_multi_bf16(const MultiAttnArgs& m, int head_dim, hipStream_t stream) {
+    int64_t blocks = 0;
+    for (int t = 0; t < m.n_targets; ++t) blocks += (int64_t)m.t[t].nqb * m.t[t].B * m.t[t].H;
+    dim3 grid((unsigned)blocks), block(128);
+    const bool oc = m.t[0].oc_full != nullptr;
+    if (head_dim == 128) {
+        if (oc) hipLaunchKernelGGL((attn_multi_bf16_kernel<128, true>), grid, block, 0, stream, m);
+        else hipLaunchKernelGGL((attn_multi_bf16_kernel<128, false>), grid, block, 0, stream, m);
+    } else {
+        if (oc) hipLaunchKernelGGL((attn_multi_bf16_kernel<64, true>), grid, block, 0, stream, m);
+        else hipLaunchKernelGGL((attn_multi_bf16_kernel<64, false>), grid, block, 0, stream, m);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStream_t stream) {
     const int64_t nqt = dense ? (a.nq + 63) / 64 : a.nqb;

@@ -33,6 +33,17 @@ struct AttnArgs {
     int32_t oc_side;
 };
 
+// Several query scales of one cache in one attention launch: per target the
+// arguments of its own launch (the K / V pointers and strides, B, H, the
+// scale and the O_cache inputs alike in all).
+constexpr int kMaxAttnTargets = VARSPARSE_MAX_ATTN_TARGETS;   // three argument blocks fit the kernarg space
+
+struct MultiAttnArgs {
+    AttnArgs t[kMaxAttnTargets];
+    int32_t n_targets;
+};
+static_assert(sizeof(MultiAttnArgs) <= 3072, "kernel arguments stay well inside the 4 KB kernarg space");
+
 struct AttnF32Args {
     const float* q;
     const float* k;
@@ -111,6 +122,7 @@ struct JoinArgs {
 hipError_t launch_ocache_correct(const OcacheArgs& a, hipStream_t stream);
 hipError_t launch_join_lists(const JoinArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStream_t stream);
+hipError_t launch_attn_multi_bf16(const MultiAttnArgs& m, int head_dim, hipStream_t stream);
 constexpr int kPairMaxNkbHost = 4096;   // key tiles the paired-tile kernel's LDS bitmaps cover
 hipError_t launch_attn_pair_bf16(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_attn_fp32(const AttnF32Args& a, int head_dim, bool dense, hipStream_t stream);

@@ -63,6 +63,7 @@ extern "C" {
 #endif
 
 #define VARSPARSE_MAX_SCALES 32
+#define VARSPARSE_MAX_ATTN_TARGETS 3   /* query scales of one varsparse_attn_fwd_multi call */
 
 typedef struct varsparse_geom {
     int32_t n_scales;                      /* number of scales in side[]            */
@@ -331,6 +332,32 @@ int varsparse_attn_fwd_ocache(const varsparse_geom* geom, int32_t q_scale, int32
                               const int64_t strides[12], float softmax_scale, const int32_t* kv_cnt,
                               const int32_t* kv_idx, int32_t lists_per_head, const void* o_full_d,
                               const void* o_sparse_d, const int64_t d_strides[6], void* stream);
+
+/*
+ * Block-sparse attention of several query scales over one cache in one
+ * launch (SparVAR, ai.info summary, "Methodology in Plain English", first
+ * module: the lists mapped from one decision scale serve all the later
+ * scales, whose attentions are independent of one another).  For each
+ * i < n_targets, target i gets exactly (bit for bit) what varsparse_attn_fwd
+ * with dtype VARSPARSE_BF16 writes for query scale q_scales[i], with q[i],
+ * o[i], lse[i] (lse NULL, or lse[i] NULL: none), strides + 12 i, kv_cnt[i] and
+ * kv_idx[i]; when o_full_d is non-NULL, what varsparse_attn_fwd_ocache writes
+ * with the decision scale d_scale <= every q_scales[i] and its outputs
+ * o_full_d / o_sparse_d (d_strides as there; both NULL: no correction).
+ * Host arrays: q_scales, q, o, lse, kv_cnt, kv_idx (n_targets entries each),
+ * strides (12 * n_targets entries; the K and V entries 3..8 equal for every
+ * target: one cache).  1 <= n_targets <= VARSPARSE_MAX_ATTN_TARGETS; every
+ * target scale a multiple of the tile side, tile == 8, bf16, head_dim in
+ * {64, 128}; lists_per_head applies to every target.  Outputs of different
+ * targets must not overlap.  EINVAL / EUNSUPPORTED as for varsparse_attn_fwd,
+ * nothing enqueued.
+ */
+int varsparse_attn_fwd_multi(const varsparse_geom* geom, int32_t n_targets, const int32_t* q_scales, int32_t B,
+                             int32_t H, int32_t head_dim, const void* const* q, const void* k, const void* v,
+                             void* const* o, float* const* lse, const int64_t* strides, float softmax_scale,
+                             const int32_t* const* kv_cnt, const int32_t* const* kv_idx, int32_t lists_per_head,
+                             int32_t d_scale, const void* o_full_d, const void* o_sparse_d,
+                             const int64_t d_strides[6], void* stream);
 
 /* Static description of a status code. */
 /* How varsparse_join_lists combines two kept-tile sets. */

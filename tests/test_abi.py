@@ -314,3 +314,31 @@ def test_attn_ocache_validation():
     assert call(per_head=2) == _lib.EINVAL
     assert lib.varsparse_attn_fwd_ocache(_g(), 12, 9, 0, 16, 128, None, None, None, None, None, None, 0.088, None,
                                          None, 0, None, None, d6, None) == _lib.OK     # empty batch
+
+
+def test_attn_multi_validation():
+    lib = _lib.lib()
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+
+    def call(**kw):
+        n = kw.get("n", 3)
+        ts = kw.get("ts", [12, 11, 10][:max(n, 0)] or [12])
+        st = kw.get("st", GOOD12 * max(n, 1))
+        return lib.varsparse_attn_fwd_multi(
+            kw.get("g", _g()), n, (I32 * len(ts))(*ts), kw.get("B", 2), 16, kw.get("d", 128),
+            arr(*([kw.get("qp", FAKE)] * len(ts))), FAKE, FAKE, arr(*([FAKE] * len(ts))), None, _strides(st),
+            0.088, arr(*([FAKE] * len(ts))), arr(*([FAKE] * len(ts))), kw.get("per_head", 1), kw.get("D", 9),
+            kw.get("f", None), kw.get("p", None), _strides([0, 0, 128] * 2), None)
+    assert call(n=0) == _lib.EINVAL
+    assert call(n=4, ts=[12, 11, 10, 9]) == _lib.EINVAL          # more targets than one launch carries
+    assert call(ts=[12, 11, 13]) == _lib.EINVAL
+    assert call(d=96) == _lib.EUNSUPPORTED
+    assert call(g=_g(SCHEDULE_13, 4)) == _lib.EUNSUPPORTED        # 8x8 tiles only
+    assert call(per_head=2) == _lib.EINVAL
+    assert call(qp=MISALIGNED) == _lib.EINVAL
+    assert call(qp=None) == _lib.EINVAL
+    other_k = GOOD12 * 2 + [0, 0, 128, 0, 0, 256] + GOOD12[6:]
+    assert call(st=other_k) == _lib.EINVAL                        # one cache: K strides equal for every target
+    assert call(f=FAKE, p=None) == _lib.EINVAL                    # both decision outputs or neither
+    assert call(f=FAKE, p=FAKE, D=11) == _lib.EINVAL              # decision scale above target 10
+    assert call(B=0) == _lib.OK                                   # empty batch
