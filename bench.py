@@ -599,11 +599,21 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
         vs.dense_attn_fwd(qs[s], k[:, :, : nks[s]], v[:, :, : nks[s]], softmax_scale=scale, out=outs[s],
                           want_lse=False, stream=stream)
 
+    small = list(range(D))[::-1]   # the scales below the decision scale, largest first
+
+    def dense_small(one_launch=True):
+        if one_launch:   # sides 1 ... 24 in one launch, each over the cache up to its own scale
+            vs.dense_attn_fwd_multi([qs[s] for s in small], k, v, [nks[s] for s in small], softmax_scale=scale,
+                                    outs=[outs[s] for s in small], want_lse=False, stream=stream)
+        else:
+            for s in small:
+                dense_at(s)
+
     multi_out = [lists_d] + [bufs[T][0] for T in W.CS4A_TARGETS]
 
     def loop_step(fused=True):
-        for s in range(D + 1):
-            dense_at(s)
+        dense_small()
+        dense_at(D)
         # the decision scale's scores and the lists of itself and every later scale, in one launch
         vs.map_indices_multi(w.sides, w.tile, D, [D, *W.CS4A_TARGETS], w.n_sink, W.CS4A_TOP_P, q_d=qs[D], k=k,
                              scores=scores, out=multi_out, stream=stream)
@@ -630,19 +640,19 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
                               want_lse=False, d_scale=D, o_full_d=outs[D], o_sparse_d=o_sparse_d, stream=stream)
 
     def dense_step():
-        for s in range(n):
+        dense_small()
+        for s in range(D, n):
             dense_at(s)
 
     def below_d():
-        for s in range(D):
-            dense_at(s)
+        dense_small()
 
     # the four forms timed in turn, three rounds, median per form (slow clock
     # drift then affects every form alike)
     reps = max(5, args.steps // 2)
     forms = (("loop", lambda: loop_step(fused="multi")), ("loop_per_target", loop_step),
              ("loop_two_launch", lambda: loop_step(fused=False)),
-             ("dense", dense_step), ("below_d", below_d))
+             ("dense", dense_step), ("below_d", below_d), ("below_d_per_scale", lambda: dense_small(False)))
     runs = {name: [] for name, _ in forms}
     for _ in range(3):
         for name, fn in forms:
@@ -674,11 +684,12 @@ def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
             "ms_per_step_one_launch_per_target": res["loop_per_target"],
             "ms_per_step_two_launch_ocache": res["loop_two_launch"],
             "dense_below_decision_ms": res["below_d"],
+            "dense_below_decision_ms_one_launch_per_scale": res["below_d_per_scale"],
             "count_sparsity": sparsity,
-            "timed": "dense attention at sides 1..24; at 32 dense + scores + one select/map launch for 32/40/48/64 + "
+            "timed": "dense attention at sides 1..24 in one launch; at 32 dense + scores + one select/map launch for 32/40/48/64 + "
                      "block-sparse over its own selection; at 40/48/64 CSLA window mask + union, then one "
                      "block-sparse attention launch over the three with the O_cache correction in its epilogue; "
-                     "dense: all 13 scales"}
+                     "dense: all 13 scales (sides 1..24 in one launch, as in the loop)"}
 
 
 def cpu_baseline(w, q_np, k_np, v_np, cnt_h, idx_h, sizes, round_bf16, seconds):

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     attn_fwd_token,
     build_mask,
     dense_attn_fwd,
+    dense_attn_fwd_multi,
     geom_counts,
     join_lists,
     lib,

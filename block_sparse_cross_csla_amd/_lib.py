@@ -15,6 +15,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvarsparse.so")
 MAX_SCALES = 32
 MAX_ATTN_TARGETS = 3
+MAX_DENSE_TARGETS = 16
 BF16, FP32 = 0, 1
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, -1, -2, -3
 
@@ -31,6 +32,7 @@ EXPORTS = (
     "varsparse_attn_fwd_ocache",
     "varsparse_attn_fwd_multi",
     "varsparse_dense_attn_fwd",
+    "varsparse_dense_attn_fwd_multi",
     "varsparse_ocache_correct",
     "varsparse_join_lists",
     "varsparse_strerror",
@@ -79,7 +81,8 @@ def _load():
                                               P, P, PI64, P]
     lib.varsparse_attn_fwd_multi.argtypes = [PG, I32, PI32, I32, I32, I32, P, P, P, P, P, PI64, F32, P, P, I32,
                                              I32, P, P, PI64, P]
-    for name in EXPORTS[:14]:
+    lib.varsparse_dense_attn_fwd_multi.argtypes = [I32, I32, I32, I32, PI64, PI64, P, P, P, P, P, PI64, F32, P]
+    for name in EXPORTS[:15]:
         getattr(lib, name).restype = ctypes.c_int
     lib.varsparse_last_hip_error.restype = ctypes.c_int
     return lib
@@ -502,6 +505,38 @@ def dense_attn_fwd(q, k, v, softmax_scale=None, out=None, lse=None, want_lse=Tru
                                          _ptr(lse), _strides(q, k, v, out), float(scale), _stream(stream)),
            "varsparse_dense_attn_fwd")
     return out, lse
+
+
+def dense_attn_fwd_multi(qs, k, v, nks, softmax_scale=None, outs=None, lses=None, want_lse=True, stream=None):
+    """Dense attention of several query sets over prefixes of one cache in one
+    launch (bf16): target i is the attention dense_attn_fwd computes for
+    qs[i] over k[:, :, :nks[i]], v[:, :, :nks[i]], each 64-query block walked
+    in one pass.  Returns [(o, lse) per target]."""
+    n = len(qs)
+    _need(1 <= n <= MAX_DENSE_TARGETS and len(nks) == n, f"one to {MAX_DENSE_TARGETS} query sets, one length each")
+    B, H, _, d = qs[0].shape
+    if outs is None:
+        outs = [torch.empty_like(q) for q in qs]
+    if lses is None:
+        lses = [torch.empty(B, H, q.shape[2], dtype=torch.float32, device=q.device) if want_lse else None
+                for q in qs]
+    _need(len(outs) == n and len(lses) == n, "one output and one lse (or None) per target")
+    strides = []
+    for q, out, lse, nk in zip(qs, outs, lses, nks):
+        _need(q.dim() == 4 and q.shape[0] == B and q.shape[1] == H and q.shape[3] == d,
+              "every query set is [B, H, nq, head_dim] with the first's B, H and head_dim")
+        _need(1 <= int(nk), "every target attends at least one key")
+        _check_qkvo(q, k, v, out, lse, q.shape[2], int(nk), bf16_only=True)
+        strides.extend(_strides(q, k, v, out))
+    _on_gpu(*qs, k, v, *outs, *lses)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    ptrs = lambda ts: (ctypes.c_void_p * n)(*[None if t is None else t.data_ptr() for t in ts])
+    i64 = lambda vals: (ctypes.c_int64 * n)(*[int(x) for x in vals])
+    _check(_LIB.varsparse_dense_attn_fwd_multi(n, B, H, d, i64([q.shape[2] for q in qs]), i64(nks), ptrs(qs), _ptr(k),
+                                               _ptr(v), ptrs(outs), ptrs(lses),
+                                               (ctypes.c_int64 * len(strides))(*strides), float(scale),
+                                               _stream(stream)), "varsparse_dense_attn_fwd_multi")
+    return list(zip(outs, lses))
 
 
 def ocache_correct(o_full_d, o_sparse_d, o_t, side_d: int, side_t: int, stream=None):

@@ -495,6 +495,54 @@ int varsparse_dense_attn_fwd(varsparse_dtype dtype, int32_t B, int32_t H, int32_
     return hip_status(vs::launch_attn_fp32(a, head_dim, true, (hipStream_t)stream));
 }
 
+int varsparse_dense_attn_fwd_multi(int32_t n_targets, int32_t B, int32_t H, int32_t head_dim, const int64_t* nq,
+                                   const int64_t* nk, const void* const* q, const void* k, const void* v,
+                                   void* const* o, float* const* lse, const int64_t* strides, float softmax_scale,
+                                   void* stream) {
+    if (n_targets < 1 || n_targets > VARSPARSE_MAX_DENSE_TARGETS || !nq || !nk) return VARSPARSE_EINVAL;
+    if (B < 0 || H < 0) return VARSPARSE_EINVAL;
+    for (int i = 0; i < n_targets; ++i) {
+        if (nq[i] < 0 || nk[i] < 1) return VARSPARSE_EINVAL;
+        if (nk[i] >= ((int64_t)1 << 30)) return VARSPARSE_EUNSUPPORTED;
+    }
+    if (!scale_ok(softmax_scale)) return VARSPARSE_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return VARSPARSE_EUNSUPPORTED;
+    if (B == 0 || H == 0) return VARSPARSE_OK;   // empty batch: nothing to compute
+    if (!q || !o || !k || !v || !strides) return VARSPARSE_EINVAL;
+    if (!aligned16(k) || !aligned16(v)) return VARSPARSE_EINVAL;
+    vs::MultiDenseArgs m{};
+    vs::AttnArgs& a = m.base;
+    a.k = (const __bf16*)k; a.v = (const __bf16*)v;
+    a.sk_b = strides[3]; a.sk_h = strides[4]; a.sk_t = strides[5];
+    a.sv_b = strides[6]; a.sv_h = strides[7]; a.sv_t = strides[8];
+    a.B = B; a.H = H; a.scale_log2 = (float)(softmax_scale * kLog2e);
+    int64_t blocks = 0;
+    int n = 0;   // targets with queries
+    for (int i = 0; i < n_targets; ++i) {
+        const int64_t* st = strides + 12 * i;
+        if (!strides_ok(st, 12, 8)) return VARSPARSE_EINVAL;
+        for (int j = 3; j < 9; ++j)   // one cache: every target reads K and V alike
+            if (st[j] != strides[j]) return VARSPARSE_EINVAL;
+        if (!offsets_fit(nk[i], st[5], st[8], head_dim)) return VARSPARSE_EUNSUPPORTED;
+        if (nq[i] == 0) continue;
+        if (!q[i] || !o[i] || !aligned16(q[i]) || !aligned16(o[i])) return VARSPARSE_EINVAL;
+        m.wg_base[n] = (int32_t)std::min<int64_t>(blocks, 0x7fffffff);
+        blocks += ((nq[i] + 63) / 64) * B * H;
+        m.q[n] = (const __bf16*)q[i]; m.o[n] = (__bf16*)o[i]; m.lse[n] = lse != nullptr ? lse[i] : nullptr;
+        m.nq[n] = nq[i]; m.nk[n] = nk[i];
+        for (int j = 0; j < 3; ++j) {
+            m.sq[n][j] = st[j];
+            m.so[n][j] = st[9 + j];
+        }
+        ++n;
+    }
+    if (blocks > 0x7fffffff) return VARSPARSE_EINVAL;
+    if (n == 0) return VARSPARSE_OK;   // no queries: nothing to compute
+    m.n_targets = n;
+    m.wg_base[n] = (int32_t)blocks;
+    return hip_status(vs::launch_dense_multi_bf16(m, head_dim, (hipStream_t)stream));
+}
+
 int varsparse_ocache_correct(int32_t B, int32_t H, int32_t head_dim, int32_t side_d, int32_t side_t,
                              const void* o_full_d, const void* o_sparse_d, void* o_t,
                              const int64_t strides[9], void* stream) {

@@ -1059,6 +1059,34 @@ __global__ __launch_bounds__(128, 2) void attn_multi_bf16_kernel(const MultiAttn
     attn_fwd_bf16_body<D, false, false, OC, true>(m.t[t], 2 * p * m.t[t].nqb + r);
 }
 
+// Dense attention of several query sets over prefixes of one cache in one
+// launch: each workgroup runs the one-pass dense walk of attn_fwd_bf16_kernel
+// for one 64-query block of one target (bit-identical to a one-target launch
+// that walks its blocks in one pass rather than split), so a step's many
+// small dense scales cost one launch ramp and tail instead of one each.  Targets take contiguous ranges of work items in the
+// caller's order.
+template <int D>
+__global__ __launch_bounds__(128, 2) void attn_dense_multi_bf16_kernel(const MultiDenseArgs m) {
+    const int G = xcd_remap(blockIdx.x, gridDim.x);
+    int t = 0;
+#pragma unroll
+    for (int u = 1; u < kMaxDenseTargets; ++u)
+        if (u < m.n_targets && G >= m.wg_base[u]) t = u;
+    AttnArgs a = m.base;
+    a.q = m.q[t];
+    a.o = m.o[t];
+    a.lse = m.lse[t];
+    a.nq = m.nq[t];
+    a.nk = m.nk[t];
+    a.sq_b = m.sq[t][0];
+    a.sq_h = m.sq[t][1];
+    a.sq_t = m.sq[t][2];
+    a.so_b = m.so[t][0];
+    a.so_h = m.so[t][1];
+    a.so_t = m.so[t][2];
+    attn_fwd_bf16_body<D, true, false, false, true>(a, G - m.wg_base[t]);
+}
+
 // ---- dense attention over few query blocks: each block's keys split over P wave pairs
 //
 // A dense launch over a handful of 64-query blocks (the small scales of a
@@ -1595,6 +1623,13 @@ hipError_t launch_attn_multi_bf16(const MultiAttnArgs& m, int head_dim, hipStrea
         if (oc) hipLaunchKernelGGL((attn_multi_bf16_kernel<64, true>), grid, block, 0, stream, m);
         else hipLaunchKernelGGL((attn_multi_bf16_kernel<64, false>), grid, block, 0, stream, m);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_multi_bf16(const MultiDenseArgs& m, int head_dim, hipStream_t stream) {
+    dim3 grid((unsigned)m.wg_base[m.n_targets]), block(128);
+    if (head_dim == 128) hipLaunchKernelGGL(attn_dense_multi_bf16_kernel<128>, grid, block, 0, stream, m);
+    else hipLaunchKernelGGL(attn_dense_multi_bf16_kernel<64>, grid, block, 0, stream, m);
     return hipGetLastError();
 }
 

@@ -44,6 +44,23 @@ struct MultiAttnArgs {
 };
 static_assert(sizeof(MultiAttnArgs) <= 3072, "kernel arguments stay well inside the 4 KB kernarg space");
 
+// Dense attention of several query sets over prefixes of one cache in one
+// launch (the small scales of a generation step, each over the cache of the
+// scales up to its own): per target its queries, outputs and lengths.
+constexpr int kMaxDenseTargets = VARSPARSE_MAX_DENSE_TARGETS;
+
+struct MultiDenseArgs {
+    AttnArgs base;    // k, v and their strides, B, H, the scale
+    int32_t n_targets;
+    int32_t wg_base[kMaxDenseTargets + 1];   // first workgroup of each target (prefix sums)
+    const __bf16* q[kMaxDenseTargets];
+    __bf16* o[kMaxDenseTargets];
+    float* lse[kMaxDenseTargets];
+    int64_t nq[kMaxDenseTargets], nk[kMaxDenseTargets];
+    int64_t sq[kMaxDenseTargets][3], so[kMaxDenseTargets][3];
+};
+static_assert(sizeof(MultiDenseArgs) <= 3072, "kernel arguments stay well inside the 4 KB kernarg space");
+
 struct AttnF32Args {
     const float* q;
     const float* k;
@@ -123,6 +140,7 @@ hipError_t launch_ocache_correct(const OcacheArgs& a, hipStream_t stream);
 hipError_t launch_join_lists(const JoinArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, int head_dim, bool dense, hipStream_t stream);
 hipError_t launch_attn_multi_bf16(const MultiAttnArgs& m, int head_dim, hipStream_t stream);
+hipError_t launch_dense_multi_bf16(const MultiDenseArgs& m, int head_dim, hipStream_t stream);
 constexpr int kPairMaxNkbHost = 4096;   // key tiles the paired-tile kernel's LDS bitmaps cover
 hipError_t launch_attn_pair_bf16(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_attn_fp32(const AttnF32Args& a, int head_dim, bool dense, hipStream_t stream);

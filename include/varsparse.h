@@ -64,6 +64,7 @@ extern "C" {
 
 #define VARSPARSE_MAX_SCALES 32
 #define VARSPARSE_MAX_ATTN_TARGETS 3   /* query scales of one varsparse_attn_fwd_multi call */
+#define VARSPARSE_MAX_DENSE_TARGETS 16 /* query sets of one varsparse_dense_attn_fwd_multi call */
 
 typedef struct varsparse_geom {
     int32_t n_scales;                      /* number of scales in side[]            */
@@ -358,6 +359,29 @@ int varsparse_attn_fwd_multi(const varsparse_geom* geom, int32_t n_targets, cons
                              const int32_t* const* kv_cnt, const int32_t* const* kv_idx, int32_t lists_per_head,
                              int32_t d_scale, const void* o_full_d, const void* o_sparse_d,
                              const int64_t d_strides[6], void* stream);
+
+/*
+ * Dense attention of several query sets over prefixes of one cache in one
+ * launch (SparVAR, ai.info summary, "Methodology in Plain English": the early
+ * scales are attended densely; each scale's queries see the cache of every
+ * scale up to their own).  Target i gets the dense attention that
+ * varsparse_dense_attn_fwd with dtype VARSPARSE_BF16 computes for nq[i]
+ * queries q[i] over the first nk[i] keys of k and v, into o[i] and lse[i]
+ * (lse NULL, or lse[i] NULL: none), with strides + 12 i (the K and V entries
+ * 3..8 equal for every target): every 64-query block walks its keys in one
+ * pass, so the result is bit-identical to that call wherever the call does
+ * the same (it splits a block's keys over wave pairs, summing in another
+ * order, when it has at most 512 blocks of 12 or more 32-key chunks).  Host arrays of n_targets entries: nq, nk, q,
+ * o, lse, and 12 * n_targets strides.  1 <= n_targets <=
+ * VARSPARSE_MAX_DENSE_TARGETS, nq[i] >= 0 (0: nothing for that target),
+ * nk[i] >= 1; bf16, head_dim in {64, 128}.  Outputs of different targets
+ * must not overlap.  EINVAL / EUNSUPPORTED as for varsparse_dense_attn_fwd,
+ * nothing enqueued.
+ */
+int varsparse_dense_attn_fwd_multi(int32_t n_targets, int32_t B, int32_t H, int32_t head_dim, const int64_t* nq,
+                                   const int64_t* nk, const void* const* q, const void* k, const void* v,
+                                   void* const* o, float* const* lse, const int64_t* strides, float softmax_scale,
+                                   void* stream);
 
 /* Static description of a status code. */
 /* How varsparse_join_lists combines two kept-tile sets. */

@@ -342,3 +342,28 @@ def test_attn_multi_validation():
     assert call(f=FAKE, p=None) == _lib.EINVAL                    # both decision outputs or neither
     assert call(f=FAKE, p=FAKE, D=11) == _lib.EINVAL              # decision scale above target 10
     assert call(B=0) == _lib.OK                                   # empty batch
+
+
+def test_dense_multi_validation():
+    lib = _lib.lib()
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    i64 = lambda *v: (ctypes.c_int64 * len(v))(*v)
+
+    def call(**kw):
+        nq = kw.get("nq", [64, 256])
+        n = kw.get("n", len(nq))
+        nk = kw.get("nk", [121, 341])
+        return lib.varsparse_dense_attn_fwd_multi(
+            n, kw.get("B", 2), 16, kw.get("d", 128), i64(*nq), i64(*nk), arr(*([kw.get("qp", FAKE)] * len(nq))),
+            FAKE, FAKE, arr(*([FAKE] * len(nq))), None, _strides(kw.get("st", GOOD12 * len(nq))), 0.088, None)
+    assert call(n=0) == _lib.EINVAL
+    assert call(n=17, nq=[64] * 17, nk=[64] * 17) == _lib.EINVAL    # more query sets than one launch carries
+    assert call(nk=[121, 0]) == _lib.EINVAL
+    assert call(nq=[64, -1]) == _lib.EINVAL
+    assert call(nk=[121, 1 << 30]) == _lib.EUNSUPPORTED
+    assert call(d=96) == _lib.EUNSUPPORTED
+    assert call(qp=MISALIGNED) == _lib.EINVAL
+    assert call(qp=None) == _lib.EINVAL
+    assert call(st=GOOD12 + [0, 0, 128, 0, 0, 256] + GOOD12[6:]) == _lib.EINVAL   # one cache: K strides equal
+    assert call(B=0) == _lib.OK                                                  # empty batch
+    assert call(nq=[0, 0], qp=None) == _lib.OK                                   # no queries at all

@@ -127,3 +127,67 @@ def test_against_oracle():
                                            c.cpu().numpy(), x.cpu().numpy(), 1 / math.sqrt(w.d))
         assert np.abs(o.float().cpu().numpy() - ro).max() <= 2e-2, T
         assert np.abs(lse.cpu().numpy() - rl).max() <= 2e-2, T
+
+
+def _dense_split(blocks: int, nk: int) -> bool:
+    """Whether a one-target dense launch of this size splits each block's keys
+    over wave pairs (the few-block form, which sums in another order)."""
+    nch = (nk + 31) // 32
+    return (blocks <= 256 and nch >= 24) or (blocks <= 512 and nch >= 12)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_dense_small_scales(d):
+    """The scales below the CS4A decision scale (sides 1 ... 24), each over the
+    cache of the scales up to its own, B = 2, H = 16, largest first and in
+    ascending order.  Every output and lse equals dense_attn_fwd's bit for bit
+    where that launch walks each 64-query block in one pass; where it splits
+    a block's keys over wave pairs (few blocks), both are held to the
+    oracle's float64 dense attention at 2e-2 on two heads."""
+    vs = _vs()
+    sides = W.CS4A.sides[:9]
+    offs = G.scale_offsets(sides)
+    B, H = 2, 16
+    q_all, k, v = gaussian(61 + d, 10, B, H, int(offs[-1]), int(offs[-1]), d)
+    kd, vd = to_device(k), to_device(v)
+    qs = [to_device(q_all[:, :, offs[s]:offs[s + 1]].copy()) for s in range(len(sides))]
+    nks = [int(offs[s + 1]) for s in range(len(sides))]
+    bh = [(0, 0), (1, H - 1)]
+    for order in (list(range(len(sides)))[::-1], list(range(len(sides)))):
+        got = vs.dense_attn_fwd_multi([qs[s] for s in order], kd, vd, [nks[s] for s in order])
+        torch.cuda.synchronize()
+        for s, (o, lse) in zip(order, got):
+            ro, rl = vs.dense_attn_fwd(qs[s], kd[:, :, : nks[s]], vd[:, :, : nks[s]])
+            torch.cuda.synchronize()
+            if not _dense_split(-(-sides[s] ** 2 // 64) * B * H, nks[s]):
+                _same(o, ro, f"o of scale {s}")
+                _same(lse, rl, f"lse of scale {s}")
+                continue
+            q = q_all[:, :, offs[s]:offs[s + 1]]
+            xo, xl = OA.dense_attention(q, k[:, :, : nks[s]], v[:, :, : nks[s]], 1 / math.sqrt(d), bh=bh)
+            for b, h in bh:
+                for name, oo, ll in (("multi", o, lse), ("one-target", ro, rl)):
+                    assert np.abs(oo[b, h].float().cpu().numpy() - xo[b, h]).max() <= 2e-2, (name, s, b, h)
+                    assert np.abs(ll[b, h].cpu().numpy() - xl[b, h]).max() <= 2e-2, (name, s, b, h)
+
+
+def test_dense_multi_against_oracle():
+    """Three query sets (1, 100 and 300 queries: partial 64-query blocks) over
+    cache prefixes of 7, 150 and 1000 keys, B = 1, H = 3, with and without
+    lse: against the oracle's float64 dense attention at 2e-2."""
+    vs = _vs()
+    nqs, nks = (1, 100, 300), (7, 150, 1000)
+    q_all, k, v = gaussian(71, 11, 1, 3, sum(nqs), max(nks), 128)
+    kd, vd = to_device(k), to_device(v)
+    qs, off = [], 0
+    for n in nqs:
+        qs.append(q_all[:, :, off:off + n].copy())
+        off += n
+    lses = [None] + [torch.empty(1, 3, n, dtype=torch.float32, device="cuda") for n in nqs[1:]]
+    got = vs.dense_attn_fwd_multi([to_device(q) for q in qs], kd, vd, nks, lses=lses)
+    torch.cuda.synchronize()
+    for q, nk, (o, lse) in zip(qs, nks, got):
+        ro, rl = OA.dense_attention(q, k[:, :, :nk], v[:, :, :nk], 1 / math.sqrt(128))
+        assert np.abs(o.float().cpu().numpy() - ro).max() <= 2e-2, nk
+        if lse is not None:
+            assert np.abs(lse.cpu().numpy() - rl).max() <= 2e-2, nk
