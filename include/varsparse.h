@@ -244,7 +244,11 @@ int varsparse_map_indices_multi(const varsparse_geom* geom, int32_t d_scale, int
  * query tiles 2p and 2p + 1 share one workgroup that walks the union of
  * their kept-tile lists, loads every key chunk once for both and attends
  * each tile to its own list only.  tile == 8, head_dim in {64, 128}; at
- * most 4096 key tiles (VARSPARSE_EUNSUPPORTED above).
+ * most 4096 key tiles (VARSPARSE_EUNSUPPORTED above).  On MI355X this form
+ * measures 0.8-0.9x the speed of varsparse_attn_fwd on the last-scale
+ * workload (a chunk kept by one tile of the pair idles the other tile's
+ * waves at its barrier), so every other path uses the 64-query kernel; it
+ * is kept to compare the pages' two block sizes, not as their setting.
  */
 int varsparse_attn_fwd_pair(const varsparse_geom* geom, int32_t q_scale, int32_t B, int32_t H, int32_t head_dim,
                             const void* q, const void* k, const void* v, void* o, float* lse,
