@@ -561,7 +561,80 @@ def bench_budget_sweep(vs, torch, W, SpatialField, to_dev, args, stream, dev):
         del q, k, v, o
     return {"workload": "last_two_8b (B=2, H=28, d=128, sides 48 and 64, budget mode 75/85/90/95%)", "points": out,
             "timed": "budget mask + attention steps; the attention alone; the dense kernel, HIP events around "
-                     "back-to-back runs"}
+                     "back-to-back runs", "both_scales": bench_last_two_joint(vs, torch, W, SpatialField, to_dev,
+                                                                               stream, dev)}
+
+
+def bench_last_two_joint(vs, torch, W, SpatialField, to_dev, stream, dev):
+    """The last two scales of the 8B shape as one step over one cache (the
+    side-64 workload's 13-scale cache; side 48 attends to its first 6425
+    tokens): both budget masks, then both attentions in one launch
+    (varsparse_attn_fwd_multi), against the same two attentions as two
+    launches and against dense attention at both sides; the budgets paired
+    by sparsity (75/85/90/95%)."""
+    w48, w64 = W.LAST_TWO_8B_48, W.LAST_TWO_8B_64
+    f = SpatialField(w64.seed, w64.wid, w64.B, w64.H, w64.d)
+    k_np, v_np = f.keys_values(w64.sides[: w64.q_scale + 1], w64.n_sink, largest_side=w64.sides[w64.q_scale])
+    k, v = to_dev(k_np), to_dev(v_np)
+    del k_np, v_np
+    ws = (w64, w48)   # largest first in the one launch
+    qs = [to_dev(f.queries(w.sides[w.q_scale])) for w in ws]
+    outs = [torch.empty_like(q) for q in qs]
+    scale = 1.0 / math.sqrt(w64.d)
+    geo = [vs.geom_counts(w.sides, w.tile, w.q_scale) for w in ws]
+    lists = [(torch.empty(g[0], dtype=torch.int32, device=dev), torch.empty(g[0], g[1], dtype=torch.int32, device=dev))
+             for g in geo]
+
+    def run(fn, warm, reps):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def dense():
+        for w, q, o, g in zip(ws, qs, outs, geo):
+            vs.dense_attn_fwd(q, k[:, :, : g[3]], v[:, :, : g[3]], softmax_scale=scale, out=o, want_lse=False,
+                              stream=stream)
+
+    dense_ms = run(dense, 2, 10)
+    dense_flops = sum(4.0 * w.d * g[2] * g[3] * w.B * w.H for w, g in zip(ws, geo))
+    points = []
+    for b64, b48 in zip(w64.budgets, w48.budgets):
+        def masks():
+            for w, budget, (c, i) in zip(ws, (b64, b48), lists):
+                vs.build_mask(w.sides, w.tile, w.q_scale, w.n_sink, budget=budget, out=(c, i, None), stream=stream)
+
+        def step(one_launch=True):
+            masks()
+            if one_launch:
+                vs.attn_fwd_multi(qs, k, v, w64.sides, w64.tile, [w.q_scale for w in ws], lists,
+                                  softmax_scale=scale, outs=outs, want_lse=False, stream=stream)
+                return
+            for w, q, o, (c, i) in zip(ws, qs, outs, lists):
+                vs.attn_fwd(q, k, v, w.sides, w.tile, w.q_scale, c, i, softmax_scale=scale, out=o, want_lse=False,
+                            stream=stream)
+
+        one = run(step, 10, 50)
+        two = run(lambda: step(False), 10, 50)
+        masks()
+        torch.cuda.synchronize()
+        flops = 0.0
+        for w, (c, i) in zip(ws, lists):
+            flops += kept_flops(c.cpu().numpy(), i.cpu().numpy(), tile_sizes(w.sides, w.q_scale, w.tile),
+                                w.tile * w.tile, w.d, w.B * w.H)
+        points.append({"budget_tiles": {"64": b64, "48": b48}, "flop_sparsity": float(1.0 - flops / dense_flops),
+                       "ms_per_step": one, "ms_per_step_two_attention_launches": two, "dense_ms": dense_ms,
+                       "effective_tflops": flops / (one * 1e-3) / 1e12, "speedup_vs_dense": dense_ms / one})
+    del k, v, qs, outs
+    return {"workload": "last_two_8b sides 64 and 48 in one step over one cache",
+            "timed": "two budget masks + both attentions in one launch (or two); dense: both sides, two launches",
+            "points": points}
 
 
 def bench_scale_loop(vs, torch, W, SpatialField, to_dev, args, stream, dev):
